@@ -1,0 +1,40 @@
+"""CPU oracle for the fused attention forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, float64 numpy code that states what the forward pass computes,
+so the HIP path can be checked against it.  Only the test suite, the smoke
+check in ``__graft_entry__`` and the ``cpu_baseline`` leg of ``bench.py``
+may import it; the library and its Python binding never do, and this
+package imports nothing from them.
+
+Pages it follows (cited by title and section throughout):
+
+* "From theory to implementation: the three FlashAttention generations
+  dissected with Triton" (su666666.com news 140181) -- sections 2.1 (online
+  softmax update), 3.1 (per-block causal mask), 4.1 (FP8 with dynamic
+  scales).
+* "Core principles behind FlashAttention's speed-up" (codearts.csdn.net)
+  -- section 1.1 (tiled double loop), 1.2 (fused kernel), 1.3 (online softmax
+  renormalisation), 4.2 (``softmax_scale = 1/sqrt(dim)``).
+* "Flash Attention" tag page (guijiagi.com/tags/flash-attention) -- the
+  excerpts on what FlashAttention solves (``S = QK^T/sqrt(d)``,
+  ``P = softmax(S)``, ``O = PV``), on the performance bottleneck (online
+  softmax over blocks, V2 deferred rescale) and on the standard attention
+  listing (``(batch, heads, seq, dim)`` layout).
+
+Modules:
+
+* ``attention`` -- the definition: scores materialised in float64, explicit
+  causal mask, two-pass softmax, ``O = P V`` and the per-row logsumexp.
+* ``fp8`` -- the OCP e4m3fn codec and the per-64-row-tile dynamic scaling.
+* ``online`` -- the pages' block-by-block online-softmax recurrences, used
+  only to cross-check the two-pass definition.
+"""
+from .attention import attention, attention_fp8, scores_rows
+from .fp8 import decode_e4m3, encode_e4m3, quantize_tiles, E4M3_MAX, TILE_ROWS
+from .online import online_softmax_attention, online_softmax_eager
+
+__all__ = [
+    "attention", "attention_fp8", "scores_rows",
+    "decode_e4m3", "encode_e4m3", "quantize_tiles", "E4M3_MAX", "TILE_ROWS",
+    "online_softmax_attention", "online_softmax_eager",
+]
