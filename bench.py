@@ -1,0 +1,203 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one ``fa_fwd`` call over the whole long-sequence workload
+(bf16, causal, B=1, H=32, N=16384, d=128; inputs resident in HBM before the
+timed region).  Prints ONE JSON line with attention TFLOP/s (4*B*H*N^2*d,
+halved for causal), ms per call, the roofline entry of the attention kernel
+and the float64 CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4_bf16]
+                    [--no-cpu-baseline] [--calib-copy-mib M]
+
+``--calib-copy-mib`` runs, after the timed loop, a plain device copy of M MiB
+so that a counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) sees a kernel
+of known traffic next to the attention kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOPS & % MFMA peak (bf16 causal N=16K d=128); ms/call"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_13_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_api.cpp")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_bf16_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s: float):
+    """Time the oracle, as it stands, on rows spread evenly over the workload until ~budget_s."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing or no BLAS info
+        threads = 1
+    rows_per_chunk = 256
+    stride = max(1, w.N // 1024)
+    t0 = time.perf_counter()
+    done = 0
+    heads = 0
+    for h in range(w.B * w.H):
+        b, hh = divmod(h, w.H)
+        rows = np.arange(h % stride, w.N, stride)
+        for s in range(0, len(rows), rows_per_chunk):
+            oracle.attention(q[b:b + 1, hh:hh + 1], k[b:b + 1, hh:hh + 1], v[b:b + 1, hh:hh + 1],
+                             w.causal, w.softmax_scale, rows=rows[s:s + rows_per_chunk])
+            done += len(rows[s:s + rows_per_chunk])
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() * done / (w.B * w.H * w.N)      # same counting convention, pro rata per row
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query rows (every {stride}th row of {heads} head(s), all {w.N} keys each, "
+                      f"float64 numpy) in {dt:.1f} s; TFLOP/s counted like the GPU figure, pro rata per row",
+            "seconds": round(dt, 2), "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "heads shard independently across GPUs, so per-GPU throughput is the single-GPU figure.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tiled_attention_13_amd import fwd, load
+    from tiled_attention_13_amd.inputs import WORKLOADS, digest, make_inputs
+
+    load()
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = WORKLOADS[args.workload]
+    t_gen = time.perf_counter()
+    q, k, v = make_inputs(w)
+    gen_s = time.perf_counter() - t_gen
+    tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    dq, dk, dv = (torch.from_numpy(a).to("cuda").to(tdt) for a in (q, k, v))
+    out = torch.empty_like(dq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        fwd(dq, dk, dv, causal=w.causal, dtype=w.dtype, out=out, lse=lse)
+    torch.cuda.synchronize()
+
+    # timed region: K calls back to back; per-call events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_all0.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        fwd(dq, dk, dv, causal=w.causal, dtype=w.dtype, out=out, lse=lse)
+        ends[i].record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_all0.elapsed_time(t_all1)
+    per_call = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    ms_per_step = total_ms / args.steps
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    kern_ms = float(per_call.mean())
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "seed": w.seed, "inputs": w.note, "parallelism": "single GPU"},
+        "pct_mfma_peak": round(100.0 * value / peak, 2),
+        "ms_per_call": {"mean": round(kern_ms, 4), "p10": round(float(np.percentile(per_call, 10)), 4),
+                        "median": round(float(np.median(per_call)), 4),
+                        "p90": round(float(np.percentile(per_call, 90)), 4)},
+        "hbm_gbps_compulsory": round(w.compulsory_bytes() / (kern_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "fa_fwd (fwd_kernel<128, causal, bf16>)",
+                     "per_launch_flops": flops},
+        "input_sha256": digest(q, k, v)[:16],
+        "input_gen_s": round(gen_s, 2),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

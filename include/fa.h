@@ -1,0 +1,134 @@
+/*
+ * fa.h -- C ABI of the fused attention forward pass for MI355X (gfx950).
+ *
+ * The operation is FlashAttention's forward pass:
+ *
+ *     O   = softmax(softmax_scale * Q K^T  [causally masked]) V
+ *     lse = per-row natural log of the softmax denominator, i.e.
+ *           lse_i = ln sum_j exp(softmax_scale * q_i . k_j) over unmasked j
+ *
+ * computed tile by tile with an online softmax (running max m and running
+ * sum l, partial O rescaled as the max grows), so the N x N score matrix
+ * never reaches device memory.  Pages defining it:
+ *   - "Flash Attention" tag page (guijiagi.com): excerpt on what
+ *     FlashAttention solves (S = QK^T/sqrt(d), P = softmax(S), O = PV), the
+ *     excerpt on the performance bottleneck (online softmax over blocks,
+ *     deferred rescale, parallelism over batch and heads) and the standard
+ *     attention listing ((batch, heads, seq, dim) layout);
+ *   - "From theory to implementation: the three FlashAttention generations
+ *     dissected with Triton": section 2.1 (running max / sum update),
+ *     3.1 (per-block causal mask), 4.1 (FP8 with dynamic per-block scales);
+ *   - "Core principles behind FlashAttention's speed-up": section 1.2
+ *     (one fused kernel), 1.3 (online renormalisation), 4.2
+ *     (softmax_scale, conventionally 1/sqrt(dim)).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, contiguous, row-major [B, H, N, d] (batch, heads,
+ *     sequence, head dim) in device memory.  Base pointers of q, k, v, o,
+ *     q8, k8 must be 16-byte aligned; lse and scale pointers 4-byte aligned.
+ *   - Supported head dims: d in {32, 64, 128}.  Any N >= 1 (tails are
+ *     masked); B, H >= 1; B*H*N*d < 2^31.
+ *   - Causal masking keeps key j for query i iff j <= i (square attention,
+ *     Nq = Nk = N).
+ *   - lse is float32 [B, H, N] and may be NULL (then it is not written).
+ *   - The caller owns every buffer; the library never frees or keeps them.
+ *     o must not alias q, k or v.  No state is kept between calls; calls on
+ *     different streams may run concurrently.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it and the call returns without synchronising; faults during
+ *     execution surface at the caller's next synchronisation on it.
+ *   - Arguments are validated before any HIP call, so argument errors are
+ *     reported synchronously (also on a machine with no GPU).  No
+ *     exceptions, aborts or prints cross this ABI.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+    FA_F32 = 0,       /* q, k, v, o float32; products and softmax in fp32 */
+    FA_BF16 = 1,      /* q, k, v, o bfloat16; fp32 accumulation */
+    FA_FP8_E4M3 = 2   /* q, k, v, o bfloat16 on input; Q and K quantised to
+                         e4m3fn per 64-row tile inside the call (see
+                         fa_quant_fp8_e4m3), V and P*V stay bf16 */
+} fa_dtype;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL_POINTER = 1,
+    FA_ERR_INVALID_SHAPE = 2,
+    FA_ERR_UNSUPPORTED_HEAD_DIM = 3,
+    FA_ERR_INVALID_SCALE = 4,
+    FA_ERR_INVALID_DTYPE = 5,
+    FA_ERR_MISALIGNED = 6,
+    FA_ERR_INVALID_ARGUMENT = 7,
+    FA_ERR_UNSUPPORTED_ARCH = 8,
+    FA_ERR_OUT_OF_MEMORY = 9,
+    FA_ERR_LAUNCH = 10,
+    FA_ERR_HIP = 11
+} fa_status;
+
+/*
+ * fa_fwd -- fused attention forward.
+ *   q, k, v : inputs [B,H,N,d] of the element type named by `dtype`.
+ *   o       : output [B,H,N,d], same element type as q (bf16 for FP8).
+ *   lse     : output float32 [B,H,N] or NULL.
+ *   causal  : 0 or 1.
+ *   softmax_scale : finite and > 0; multiplies the fp32 scores (it is not
+ *             folded into the stored Q).
+ *   dtype   : FA_F32, FA_BF16 or FA_FP8_E4M3.  For FA_FP8_E4M3 the call
+ *             allocates a stream-ordered workspace (hipMallocAsync /
+ *             hipFreeAsync on `stream`) for the quantised Q, K and their
+ *             scales, runs fa_quant_fp8_e4m3 on q and k, then the FP8 kernel.
+ * Returns FA_OK or the first error found.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int64_t B, int64_t H, int64_t N, int64_t d,
+                 int causal, float softmax_scale, fa_dtype dtype, void* stream);
+
+/*
+ * fa_quant_fp8_e4m3 -- per-tile dynamic FP8 quantisation (Triton walkthrough
+ * page, section 4.1: a scale from the block's largest magnitude; here with
+ * the e4m3fn range 448 and 64-row tiles).
+ *   x_bf16 : input bf16 [BH, N, d] (BH = B*H independent slices).
+ *   x8     : output e4m3fn codes, bytes [BH, N, d].
+ *   scale  : output float32 [BH, ceil(N/64)].
+ * For every slice and tile t of rows [64t, min(64t+64, N)):
+ *   amax = max |x| over the tile;  scale_t = 448.0f / max(amax, 1e-6f)
+ *   (IEEE fp32 division);  code = e4m3fn_RNE(clamp(fp32(x * scale_t), +-448)).
+ * Dequantisation is x ~= decode(code) / scale_t.
+ */
+fa_status fa_quant_fp8_e4m3(const void* x_bf16, uint8_t* x8, float* scale,
+                            int64_t BH, int64_t N, int64_t d, void* stream);
+
+/*
+ * fa_fwd_fp8 -- attention forward on already-quantised Q and K.
+ *   q8, k8   : e4m3fn codes [B,H,N,d];  q_scale, k_scale : float32
+ *              [B,H,ceil(N/64)] as written by fa_quant_fp8_e4m3.
+ *   v_bf16   : bf16 [B,H,N,d];  o_bf16 : bf16 output [B,H,N,d];  lse as above.
+ * Scores are softmax_scale * (q8 . k8) / (q_scale[i/64] * k_scale[j/64]),
+ * the products taken on e4m3 matrix cores with fp32 accumulation.
+ */
+fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                     const void* v_bf16, void* o_bf16, float* lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d,
+                     int causal, float softmax_scale, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_string(fa_status s);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

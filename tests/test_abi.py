@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every entry point of include/fa.h, and
+rejects bad arguments before touching HIP (so these run without a GPU).
+
+No call here ever carries a complete, valid argument set: every call fails
+validation, so no kernel is launched and no pointer is dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tiled_attention_13_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FAKE = 0x100000          # 16-byte aligned, never dereferenced (validation fails first)
+OK_ARGS = dict(q=FAKE, k=FAKE + 0x1000, v=FAKE + 0x2000, o=FAKE + 0x3000, lse=FAKE + 0x4000,
+               B=1, H=2, N=128, d=64, causal=0, scale=0.125, dtype=1)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.lib_path()):
+        pytest.fail("libfa.so is not built (run `python -m tiled_attention_13_amd.build`)")
+    return _binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(_binding.SIGNATURES), declared
+    raw = ctypes.CDLL(_binding.lib_path())
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+FA_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.fa_abi_version() == int(m.group(1))
+
+
+def test_status_strings_cover_every_code(lib):
+    codes = [int(x) for x in re.findall(r"FA_[A-Z0-9_]+\s*=\s*(\d+)", open(HEADER).read())]
+    for c in range(max(codes) + 1):
+        s = lib.fa_status_string(c).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_string(999).decode() == "unknown status"
+
+
+def _fwd(lib, **over):
+    a = dict(OK_ARGS, **over)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1),
+    (dict(B=0), 2), (dict(H=-1), 2), (dict(N=0), 2), (dict(d=0), 2),
+    (dict(B=1 << 20, H=1 << 10, N=1 << 10, d=64), 2),
+    (dict(d=48), 3), (dict(d=256), 3), (dict(d=16), 3),
+    (dict(scale=0.0), 4), (dict(scale=-1.0), 4), (dict(scale=float("inf")), 4), (dict(scale=float("nan")), 4),
+    (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(causal=2), 7), (dict(o=FAKE), 7),
+    (dict(q=FAKE + 8), 6), (dict(o=FAKE + 0x3004), 6), (dict(lse=FAKE + 0x4002), 6),
+])
+def test_fa_fwd_rejects_bad_arguments(lib, over, status):
+    # each case also carries one invalid argument, so validation returns before any HIP call
+    assert _fwd(lib, **over) == status
+
+
+def test_fa_fwd_fp8_and_quant_reject_bad_arguments(lib):
+    P = FAKE
+    f = lib.fa_fwd_fp8
+    assert f(0, P, P, P, P, P + 0x100, None, 1, 1, 64, 64, 0, 0.1, None) == 1
+    assert f(P, P, P, P, P, P + 0x100, None, 1, 1, 64, 40, 0, 0.1, None) == 3
+    assert f(P, P, P, P, P, P + 0x100, None, 1, 1, 64, 64, 0, -0.1, None) == 4
+    assert f(P, P, P, P, P, P + 0x100, None, 1, 1, 64, 64, 3, 0.1, None) == 7
+    assert f(P, P + 2, P, P, P, P + 0x100, None, 1, 1, 64, 64, 0, 0.1, None) == 6
+    q = lib.fa_quant_fp8_e4m3
+    assert q(0, P, P, 1, 64, 64, None) == 1
+    assert q(P, P, P, 0, 64, 64, None) == 2
+    assert q(P, P, P, 1, 64, 96, None) == 3
+    assert q(P + 4, P, P, 1, 64, 64, None) == 6
+
+
+def test_python_wrapper_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "_LIB_PATH", "/nonexistent/libfa.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        _binding.load()

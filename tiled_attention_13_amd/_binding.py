@@ -1,0 +1,152 @@
+"""ctypes binding of ``libfa.so`` (the C ABI in ``include/fa.h``).
+
+Argument marshalling only: tensors are passed as raw device pointers with
+the current torch stream; every step of the forward pass runs in the HIP
+kernels.  There is no fallback: if the library is missing or the call fails,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+DTYPE_CODES = {"f32": FA_F32, "bf16": FA_BF16, "fp8": FA_FP8_E4M3}
+
+# (name, restype, argtypes) of every entry point declared in include/fa.h
+_P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
+    "fa_quant_fp8_e4m3": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _P]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+    "fa_abi_version": (_I, []),
+}
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed with status {status}: {status_string(status)}")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
+                               "(run `python -m tiled_attention_13_amd.build`)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FAError(status, where)
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _check_qkv(q, k, v, torch_dtype):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dtype != torch_dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {torch_dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+        if t.dim() != 4 or t.shape != q.shape:
+            raise ValueError("q, k, v must share one [B, H, N, d] shape")
+
+
+def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None, dtype: str | None = None,
+        out=None, lse=None, with_lse: bool = True, stream=None):
+    """Fused attention forward through ``fa_fwd``.
+
+    q, k, v: contiguous device tensors ``[B, H, N, d]`` (float32 for
+    dtype "f32", bfloat16 for "bf16" and "fp8"; "fp8" quantises Q and K to
+    e4m3 per 64-row tile inside the call).  ``softmax_scale`` defaults to
+    ``1/sqrt(d)``.  Returns ``(o, lse)`` (lse is None when ``with_lse`` is
+    False and no ``lse`` buffer is given).
+    """
+    import torch
+    if dtype is None:
+        dtype = "f32" if q.dtype == torch.float32 else "bf16"
+    code = DTYPE_CODES[dtype]
+    _check_qkv(q, k, v, torch.float32 if dtype == "f32" else torch.bfloat16)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                       int(bool(causal)), scale, code, _stream_ptr(stream))
+    _check(st, "fa_fwd")
+    return out, lse
+
+
+def quant_fp8(x, stream=None):
+    """Per-64-row-tile e4m3fn quantisation of a bf16 ``[B, H, N, d]`` tensor.
+
+    Returns ``(codes uint8 [B,H,N,d], scale float32 [B,H,ceil(N/64)])``.
+    """
+    import torch
+    if not x.is_cuda or x.dtype != torch.bfloat16 or not x.is_contiguous() or x.dim() != 4:
+        raise ValueError("x must be a contiguous bf16 device tensor [B, H, N, d]")
+    B, H, N, d = x.shape
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty((B, H, (N + 63) // 64), dtype=torch.float32, device=x.device)
+    st = load().fa_quant_fp8_e4m3(_ptr(x), _ptr(codes), _ptr(scale), B * H, N, d, _stream_ptr(stream))
+    _check(st, "fa_quant_fp8_e4m3")
+    return codes, scale
+
+
+def fwd_fp8(q8, q_scale, k8, k_scale, v, causal: bool = False, softmax_scale: float | None = None,
+            out=None, lse=None, with_lse: bool = True, stream=None):
+    """Attention forward on pre-quantised e4m3 Q/K (``fa_fwd_fp8``); V and O bf16."""
+    import torch
+    B, H, N, d = v.shape
+    for name, t, dt in (("q8", q8, torch.uint8), ("k8", k8, torch.uint8), ("v", v, torch.bfloat16),
+                        ("q_scale", q_scale, torch.float32), ("k_scale", k_scale, torch.float32)):
+        if not t.is_cuda or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    if q8.shape != v.shape or k8.shape != v.shape:
+        raise ValueError("q8, k8, v must share one [B, H, N, d] shape")
+    if q_scale.shape != (B, H, (N + 63) // 64) or k_scale.shape != q_scale.shape:
+        raise ValueError("scales must be [B, H, ceil(N/64)]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(v)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=v.device)
+    st = load().fa_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(out), _ptr(lse),
+                           B, H, N, d, int(bool(causal)), scale, _stream_ptr(stream))
+    _check(st, "fa_fwd_fp8")
+    return out, lse

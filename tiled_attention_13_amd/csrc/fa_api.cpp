@@ -1,0 +1,165 @@
+// C ABI of the attention forward library (declared in include/fa.h).
+//
+// Every argument is checked before the first HIP call, so argument errors come
+// back synchronously and can be exercised on a machine without a GPU.  After
+// validation the call checks (once per device) that it runs on gfx950 and
+// enqueues the kernels on the caller's stream.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_state[kMaxDevices];
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_SHAPE;
+    if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
+    // element offsets inside a launch are formed in 32-bit arithmetic per (b, h)
+    // slice and 64-bit across slices; keep the whole tensor below 2^31 elements
+    const long double total = static_cast<long double>(B) * H * N * d;
+    if (total >= 2147483648.0L) return FA_ERR_INVALID_SHAPE;
+    return FA_OK;
+}
+
+fa_status check_scale(float s) {
+    if (!std::isfinite(s) || !(s > 0.0f)) return FA_ERR_INVALID_SCALE;
+    return FA_OK;
+}
+
+fa_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED_ARCH;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FA_ERR_HIP;
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? FA_OK : FA_ERR_UNSUPPORTED_ARCH;
+}
+
+fa_status launch_status(hipError_t e) {
+    if (e == hipSuccess) return FA_OK;
+    if (e == hipErrorOutOfMemory) return FA_ERR_OUT_OF_MEMORY;
+    return FA_ERR_LAUNCH;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+    switch (s) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case FA_ERR_INVALID_SHAPE: return "B, H, N must be >= 1 and B*H*N*d < 2^31";
+        case FA_ERR_UNSUPPORTED_HEAD_DIM: return "head dim must be 32, 64 or 128";
+        case FA_ERR_INVALID_SCALE: return "softmax_scale must be finite and > 0";
+        case FA_ERR_INVALID_DTYPE: return "unknown dtype";
+        case FA_ERR_MISALIGNED: return "tensor pointers must be 16-byte aligned (lse/scales 4-byte)";
+        case FA_ERR_INVALID_ARGUMENT: return "invalid argument (causal must be 0 or 1; o must not alias inputs)";
+        case FA_ERR_UNSUPPORTED_ARCH: return "current device is not gfx950 (MI355X)";
+        case FA_ERR_OUT_OF_MEMORY: return "device workspace allocation failed";
+        case FA_ERR_LAUNCH: return "kernel launch failed";
+        case FA_ERR_HIP: return "HIP runtime call failed";
+    }
+    return "unknown status";
+}
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+fa_status fa_quant_fp8_e4m3(const void* x_bf16, uint8_t* x8, float* scale, int64_t BH, int64_t N, int64_t d,
+                            void* stream) {
+    if (!x_bf16 || !x8 || !scale) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(1, BH, N, d);
+    if (st != FA_OK) return st;
+    if (!aligned(x_bf16, 16) || !aligned(x8, 16) || !aligned(scale, 4)) return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    return launch_status(fa::launch_quant_fp8(x_bf16, x8, scale, static_cast<int>(BH), static_cast<int>(N),
+                                              static_cast<int>(d), static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
+                     const void* v_bf16, void* o_bf16, float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int causal, float softmax_scale, void* stream) {
+    if (!q8 || !q_scale || !k8 || !k_scale || !v_bf16 || !o_bf16) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    if (o_bf16 == q8 || o_bf16 == k8 || o_bf16 == v_bf16) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q8, 16) || !aligned(k8, 16) || !aligned(v_bf16, 16) || !aligned(o_bf16, 16) ||
+        !aligned(q_scale, 4) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    fa::FwdArgs a{fa::Kind::FP8, q8, k8, v_bf16, o_bf16, lse, q_scale, k_scale,
+                  static_cast<int>(B * H), static_cast<int>(N), static_cast<int>(d), causal == 1, softmax_scale};
+    return launch_status(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+                 int64_t d, int causal, float softmax_scale, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_DTYPE;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    if (o == q || o == k || o == v) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    if (dtype != FA_FP8_E4M3) {
+        fa::FwdArgs a{dtype == FA_F32 ? fa::Kind::F32 : fa::Kind::BF16, q, k, v, o, lse, nullptr, nullptr,
+                      BH, n, dd, causal == 1, softmax_scale};
+        return launch_status(fa::launch_fwd(a, s));
+    }
+
+    // FP8: stream-ordered workspace for the e4m3 codes of Q and K and their scales
+    const size_t codes = static_cast<size_t>(BH) * n * dd;
+    const size_t n_scales = static_cast<size_t>(BH) * ((n + 63) / 64);
+    const size_t off_k8 = round_up(codes, 256);
+    const size_t off_qs = off_k8 + round_up(codes, 256);
+    const size_t off_ks = off_qs + round_up(n_scales * 4, 256);
+    const size_t total = off_ks + round_up(n_scales * 4, 256);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return FA_ERR_OUT_OF_MEMORY;
+    }
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint8_t* q8 = base;
+    uint8_t* k8 = base + off_k8;
+    float* qs = reinterpret_cast<float*>(base + off_qs);
+    float* ks = reinterpret_cast<float*>(base + off_ks);
+    hipError_t e = fa::launch_quant_fp8(q, q8, qs, BH, n, dd, s);
+    if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, ks, BH, n, dd, s);
+    if (e == hipSuccess) {
+        fa::FwdArgs a{fa::Kind::FP8, q8, k8, v, o, lse, qs, ks, BH, n, dd, causal == 1, softmax_scale};
+        e = fa::launch_fwd(a, s);
+    }
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return launch_status(e);
+    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

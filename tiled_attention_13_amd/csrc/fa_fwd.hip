@@ -1,0 +1,651 @@
+// Fused attention forward for gfx950 (MI355X): O = softmax(scale * Q K^T) V and lse.
+//
+// One workgroup owns a tile of BM = 128 queries of one (batch, head) and
+// walks the key/value sequence in tiles of BN keys, the tiled double loop of
+// "Core principles behind FlashAttention's speed-up" (section 1.1) in the
+// FlashAttention-2 order (parallel over batch, heads and query tiles; the
+// "Flash Attention" tag page, excerpt on V2).  Everything between loading a
+// K/V tile and writing O stays in registers and LDS (same page, section 1.2).
+//
+// Per wave: 32 queries.  Scores are produced transposed, S^T = K Q^T, on
+// 32x32 MFMAs: A = 32 keys from LDS, B = 32 queries held in registers for
+// the whole loop.  In the 32x32 accumulator layout lane l owns column
+// l % 32, so every lane holds 16 scores of ONE query (the other 16 of each
+// 32-key block sit in lane l ^ 32).  Row reductions are therefore in-lane
+// plus one v_permlane32_swap, and the probabilities already sit where the
+// B operand of the next MFMA, O^T += V^T P^T, wants them: no LDS round trip
+// for P.  V^T is produced while K/V tiles are copied into LDS.
+//
+// Online softmax (Triton walkthrough page, section 2.1): running max m and
+// running sum l per query, kept in base-2 units with softmax_scale*log2(e)
+// folded into one FMA before v_exp_f32; the accumulator is rescaled by
+// exp2(m_old - m_new) (skipped when that factor is 1 in every lane), and
+// the division by l is deferred to the epilogue (tag page, excerpt on V2).
+// l is summed from the fp32 probabilities before they are rounded to bf16.
+//
+// Causal (Triton walkthrough page, section 3.1): key tiles entirely above
+// the diagonal are never loaded, a wave skips tiles that lie above its own
+// rows, and only tiles that cross the diagonal or the sequence end compare
+// indices.  Workgroups are issued heaviest query tile first.
+//
+// FP8 (same page, section 4.1): Q and K arrive as e4m3fn codes with one
+// fp32 scale per 64-row tile; S^T runs on the 32x32x64 f8f6f4 MFMA and the
+// dequantisation 1/(q_scale*k_scale) is folded into the exp2 constant
+// (BN = 64 keeps one K scale per tile).  V and P*V stay bf16.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+struct KParams {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    uint8_t* o;
+    float* lse;
+    const float* q_scale;
+    const float* k_scale;
+    int BH;
+    int N;
+    int n_qtiles;
+    float c_log2;       // softmax_scale * log2(e)
+};
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Max / sum with the lane 32 apart (v_permlane32_swap: both halves see both values).
+__device__ __forceinline__ float max_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row of the 32x32 MFMA accumulator held in register v of a lane in half h.
+__device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+// ---------------------------------------------------------------------------
+// Online-softmax step on the scores one lane holds for its query.
+// s[NS]: scores (already masked to -inf), c: scale into base-2 units.
+// Updates m (base-2 running max) and l (this lane's part of the running sum),
+// overwrites s with the probabilities and returns the rescale factor alpha.
+// ---------------------------------------------------------------------------
+template <int NS>
+__device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m, float& l) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) mx = fmaxf(mx, s[i]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;   // nothing unmasked yet
+    const float alpha = fast_exp2(m - m_use);
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const float p = fast_exp2(fmaf(s[i], c, -m_use));
+        s[i] = p;
+        rs += p;
+    }
+    l = fmaf(l, alpha, rs);
+    m = m_new;
+    return alpha;
+}
+
+// ===========================================================================
+// bf16 / fp8 kernel
+// ===========================================================================
+template <int D, bool CAUSAL, bool FP8>
+struct Cfg {
+    static constexpr int NW = 4;                 // waves per workgroup
+    static constexpr int BM = 32 * NW;           // queries per workgroup
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int KROW = FP8 ? D + 16 : 2 * D + 16;   // bytes per K row in LDS (padded)
+    static constexpr int VROW = 2 * BN + 16;     // bytes per V^T row in LDS (padded)
+    static constexpr int KBYTES = BN * KROW;
+    static constexpr int VBYTES = D * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int K_CHUNKS = BN * (FP8 ? D : 2 * D) / 16;   // 16-byte chunks per K tile
+    static constexpr int K_CPR = (FP8 ? D : 2 * D) / 16;           // chunks per K row
+    static constexpr int K_PER_T = (K_CHUNKS + 255) / 256;
+    static constexpr int V_UNITS = (BN / 4) * (D / 8);             // 4 keys x 8 dims each
+    static constexpr int V_PER_T = (V_UNITS + 255) / 256;
+    // FP8 with D a multiple of 64 uses the 32x32x64 f8f6f4 MFMA (32 codes per
+    // lane); D = 32 uses the 32x32x16 fp8 MFMA (8 codes per lane).
+    static constexpr bool F8W = FP8 && (D % 64 == 0);
+    static constexpr bool F8N = FP8 && !F8W;
+    static constexpr int QREGS = F8W ? D / 64 : D / 16;            // k steps of S^T
+};
+
+// LDS column of key `kk` (0..63) inside a V^T row.  Keys are permuted within
+// each group of 16 so that the eight keys one lane contracts over in a P*V
+// MFMA are adjacent (one 16-byte read); see the P fragment layout below.
+__device__ __forceinline__ int vt_slot(int kk) {
+    const int c = kk >> 4, a = (kk >> 3) & 1, hh = (kk >> 2) & 1, b = kk & 3;
+    return 16 * c + 8 * hh + 4 * a + b;
+}
+
+template <int D, bool CAUSAL, bool FP8>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(KParams p) {
+    using C = Cfg<D, CAUSAL, FP8>;
+    constexpr int BM = C::BM, BN = C::BN;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+
+    int qt = blockIdx.x / p.BH;
+    const int bh = blockIdx.x - qt * p.BH;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;        // heaviest query tiles first
+    const int q0 = qt * BM;
+    const int qw0 = q0 + 32 * w;                  // this wave's first query
+    const int my_q = qw0 + l32;
+
+    const size_t slice = static_cast<size_t>(bh) * N * D;     // elements before this (b, h)
+    constexpr int QK_ES = FP8 ? 1 : 2;                         // bytes per Q/K element
+    const uint8_t* qg = p.q + slice * QK_ES;
+    const uint8_t* kg = p.k + slice * QK_ES;
+    const uint8_t* vg = p.v + slice * 2;
+
+    // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
+    u32x4 qf[C::F8W ? 2 * C::QREGS : C::QREGS];
+    {
+        const bool ok = my_q < N;
+        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * QK_ES;
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i) {
+            if constexpr (C::F8W) {
+                // 32 codes per lane per 64-wide k step: dims 64i + 32h .. +31
+                qf[2 * i] = ok ? ld16(row + 64 * i + 32 * h) : u32x4{0, 0, 0, 0};
+                qf[2 * i + 1] = ok ? ld16(row + 64 * i + 32 * h + 16) : u32x4{0, 0, 0, 0};
+            } else if constexpr (C::F8N) {
+                // 8 codes per lane per 16-wide k step: dims 16i + 8h .. +7
+                const u32x2 x = ok ? *reinterpret_cast<const u32x2*>(row + 16 * i + 8 * h) : u32x2{0, 0};
+                qf[i] = u32x4{x[0], x[1], 0, 0};
+            } else {
+                // 8 bf16 per lane per 16-wide k step: dims 16i + 8h .. +7
+                qf[i] = ok ? ld16(row + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+
+    const int n_ktiles_all = (N + BN - 1) / BN;
+    const int n_scale = (N + 63) / 64;            // FP8 scales per (b, h): one per 64 rows
+    float c_q = p.c_log2;
+    if (FP8) c_q = p.c_log2 / p.q_scale[bh * n_scale + (qw0 < N ? qw0 : N - 1) / 64];
+
+    const int q_end = min(q0 + BM, N);
+    const int n_kt = CAUSAL ? min(n_ktiles_all, (q_end + BN - 1) / BN) : n_ktiles_all;
+
+    // ---- global -> register staging of one K/V tile
+    u32x4 kst[C::K_PER_T];
+    u32x4 vst[C::V_PER_T][4];
+    auto load_tile = [&](int j) {
+        const int n0 = j * BN;
+#pragma unroll
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int c = i * 256 + tid;
+            if (c < C::K_CHUNKS) {
+                const int row = c / C::K_CPR, col = c - row * C::K_CPR;
+                const int key = n0 + row;
+                kst[i] = key < N ? ld16(kg + (static_cast<size_t>(key) * D) * QK_ES + 16 * col)
+                                 : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::V_PER_T; ++i) {
+            const int u = i * 256 + tid;
+            if (u < C::V_UNITS) {
+                const int kq = u % (BN / 4), dg = u / (BN / 4);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = n0 + 4 * kq + r;
+                    vst[i][r] = key < N ? ld16(vg + 2 * (static_cast<size_t>(key) * D + 8 * dg))
+                                        : u32x4{0, 0, 0, 0};
+                }
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        uint8_t* ks = smem + buf * C::STAGE;
+        uint8_t* vs = ks + C::KBYTES;
+#pragma unroll
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int c = i * 256 + tid;
+            if (c < C::K_CHUNKS) {
+                const int row = c / C::K_CPR, col = c - row * C::K_CPR;
+                *reinterpret_cast<u32x4*>(ks + row * C::KROW + 16 * col) = kst[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::V_PER_T; ++i) {
+            const int u = i * 256 + tid;
+            if (u < C::V_UNITS) {
+                const int kq = u % (BN / 4), dg = u / (BN / 4);
+                uint8_t* dst = vs + 2 * vt_slot(4 * kq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    // dim 8*dg+e of keys 4kq..4kq+3 -> 8 contiguous bytes of V^T
+                    const int wd = e >> 1, sh = 16 * (e & 1);
+                    const uint32_t x0 = (vst[i][0][wd] >> sh) & 0xFFFFu;
+                    const uint32_t x1 = (vst[i][1][wd] >> sh) & 0xFFFFu;
+                    const uint32_t x2 = (vst[i][2][wd] >> sh) & 0xFFFFu;
+                    const uint32_t x3 = (vst[i][3][wd] >> sh) & 0xFFFFu;
+                    *reinterpret_cast<u32x2*>(dst + (8 * dg + e) * C::VROW) =
+                        u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+                }
+            }
+        }
+    };
+
+    // ---- accumulators: O^T, lane owns query l32, dims acc_row(v, h) of each 32-dim block
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
+    float m_run = kNegInf, l_run = 0.0f;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int j = 0; j < n_kt; ++j) {
+        const int n0 = j * BN;
+        const bool more = j + 1 < n_kt;
+        if (more) load_tile(j + 1);
+
+        const bool active = !CAUSAL || n0 <= qw0 + 31;     // wave-uniform
+        if (active) {
+            const uint8_t* ks = smem + (j & 1) * C::STAGE;
+            const uint8_t* vs = ks + C::KBYTES;
+
+            // S^T for BN keys: s[kb] holds keys n0 + 32kb + acc_row(v, h)
+            f32x16 sacc[BN / 32];
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+                f32x16 acc;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+                const uint8_t* krow = ks + (32 * kb + l32) * C::KROW;
+#pragma unroll
+                for (int i = 0; i < C::QREGS; ++i) {
+                    if constexpr (C::F8W) {
+                        const u32x4 a0 = ld16(krow + 64 * i + 32 * h);
+                        const u32x4 a1 = ld16(krow + 64 * i + 32 * h + 16);
+                        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                        const u32x4 b0 = qf[2 * i], b1 = qf[2 * i + 1];
+                        const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                         (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+                        // fp8 e4m3 x fp8 e4m3, unit block scales (E8M0 127 = 2^0)
+                        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+                    } else if constexpr (C::F8N) {
+                        const long a = __builtin_bit_cast(long, *reinterpret_cast<const u32x2*>(krow + 16 * i + 8 * h));
+                        const long b = __builtin_bit_cast(long, u32x2{qf[i][0], qf[i][1]});
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, acc, 0, 0, 0);
+                    } else {
+                        const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(krow + 2 * (16 * i + 8 * h)));
+                        const bf16x8 b = __builtin_bit_cast(bf16x8, qf[i]);
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+                    }
+                }
+                sacc[kb] = acc;
+            }
+
+            float s[BN / 2];
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[16 * kb + v] = sacc[kb][v];
+
+            const bool need_mask = (CAUSAL && n0 + BN - 1 > qw0) || (n0 + BN > N);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = n0 + 32 * kb + acc_row(v, h);
+                        if (key >= N || (CAUSAL && key > my_q)) s[16 * kb + v] = kNegInf;
+                    }
+            }
+
+            float c = c_q;
+            if (FP8) c = c_q / p.k_scale[bh * n_scale + j];     // BN = 64: tile j is scale tile j
+
+            const float alpha = softmax_step(s, c, m_run, l_run);
+            if (!__all(alpha == 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+            }
+
+            // P fragments (B operand of O^T += V^T P^T) for 16-key step c:
+            // slot t of lane (l32, h) <- s[8c + t], i.e. key 16c + 8(t/4) + 4h + t%4.
+            bf16x8 pf[BN / 16];
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) pf[cc][t] = static_cast<__bf16>(s[8 * cc + t]);
+
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const uint8_t* vrow = vs + (32 * db + l32) * C::VROW;
+#pragma unroll
+                for (int cc = 0; cc < BN / 16; ++cc) {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(vrow + 2 * (16 * cc + 8 * h)));
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[cc], o[db], 0, 0, 0);
+                }
+            }
+        }
+
+        if (more) store_tile((j + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O^T / l, lse = ln2 * (m + log2 l)
+    const float l_tot = sum_halves(l_run);
+    if (my_q < N) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint8_t* orow = p.o + (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(o[db][4 * g + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + 2 * (32 * db + 8 * g + 4 * h)) = out;
+            }
+        if (p.lse != nullptr && h == 0)
+            p.lse[static_cast<size_t>(bh) * N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ===========================================================================
+// fp32 kernel: same algorithm on the 32x32x2 fp32 MFMA (no reduced-precision
+// products, probabilities kept in fp32 for P*V).
+// ===========================================================================
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_f32_kernel(KParams p) {
+    constexpr int BM = 128, BN = 32;
+    constexpr int KST = D + 1;       // floats per K row in LDS (odd stride: column reads hit distinct banks)
+    constexpr int VST = D + 4;       // floats per V row in LDS (16-byte aligned rows)
+    constexpr int STAGE = BN * KST + BN * VST;
+    constexpr int CHUNKS = BN * D / 4;                 // 16-byte chunks per K (or V) tile
+    constexpr int PER_T = (CHUNKS + 255) / 256;
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    int qt = blockIdx.x / p.BH;
+    const int bh = blockIdx.x - qt * p.BH;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;
+    const int q0 = qt * BM, qw0 = q0 + 32 * w, my_q = qw0 + l32;
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const float* qg = reinterpret_cast<const float*>(p.q) + slice;
+    const float* kg = reinterpret_cast<const float*>(p.k) + slice;
+    const float* vg = reinterpret_cast<const float*>(p.v) + slice;
+
+    float qf[D / 2];                                   // B operand: Q[my_q][2i + h]
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) qf[i] = my_q < N ? qg[static_cast<size_t>(my_q) * D + 2 * i + h] : 0.0f;
+
+    const int n_ktiles_all = (N + BN - 1) / BN;
+    const int q_end = min(q0 + BM, N);
+    const int n_kt = CAUSAL ? min(n_ktiles_all, (q_end + BN - 1) / BN) : n_ktiles_all;
+
+    f32x4 kst[PER_T], vst[PER_T];
+    auto load_tile = [&](int j) {
+        const int n0 = j * BN;
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int c = i * 256 + tid;
+            if (c < CHUNKS) {
+                const int row = c / (D / 4), col = c - row * (D / 4);
+                const int key = n0 + row;
+                const size_t off = static_cast<size_t>(key) * D + 4 * col;
+                kst[i] = key < N ? *reinterpret_cast<const f32x4*>(kg + off) : f32x4{0, 0, 0, 0};
+                vst[i] = key < N ? *reinterpret_cast<const f32x4*>(vg + off) : f32x4{0, 0, 0, 0};
+            }
+        }
+    };
+    auto store_tile = [&](int buf) {
+        float* ks = smem + buf * STAGE;
+        float* vs = ks + BN * KST;
+#pragma unroll
+        for (int i = 0; i < PER_T; ++i) {
+            const int c = i * 256 + tid;
+            if (c < CHUNKS) {
+                const int row = c / (D / 4), col = c - row * (D / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ks[row * KST + 4 * col + e] = kst[i][e];
+                *reinterpret_cast<f32x4*>(vs + row * VST + 4 * col) = vst[i];
+            }
+        }
+    };
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
+    float m_run = kNegInf, l_run = 0.0f;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int j = 0; j < n_kt; ++j) {
+        const int n0 = j * BN;
+        const bool more = j + 1 < n_kt;
+        if (more) load_tile(j + 1);
+        const bool active = !CAUSAL || n0 <= qw0 + 31;
+        if (active) {
+            const float* ks = smem + (j & 1) * STAGE;
+            const float* vs = ks + BN * KST;
+            f32x16 acc;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < D / 2; ++i)
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[l32 * KST + 2 * i + h], qf[i], acc, 0, 0, 0);
+            float s[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[v] = acc[v];
+            if ((CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = n0 + acc_row(v, h);
+                    if (key >= N || (CAUSAL && key > my_q)) s[v] = kNegInf;
+                }
+            }
+            const float alpha = softmax_step(s, p.c_log2, m_run, l_run);
+            if (!__all(alpha == 1.0f)) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+            }
+            // contraction step v: lane (l32, h) supplies P[my_q][key acc_row(v, h)]
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs[acc_row(v, h) * VST + 32 * db + l32], s[v],
+                                                                 o[db], 0, 0, 0);
+        }
+        if (more) store_tile((j + 1) & 1);
+        __syncthreads();
+    }
+
+    const float l_tot = sum_halves(l_run);
+    if (my_q < N) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        float* orow = reinterpret_cast<float*>(p.o) + slice + static_cast<size_t>(my_q) * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                f32x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = o[db][4 * g + e] * inv;
+                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * h) = out;
+            }
+        if (p.lse != nullptr && h == 0)
+            p.lse[static_cast<size_t>(bh) * N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ===========================================================================
+// Per-64-row-tile e4m3fn quantisation (one workgroup per tile)
+// ===========================================================================
+
+// e4m3fn code of a finite fp32 value with |y| <= 448, rounded to nearest even.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    const uint32_t bits = __float_as_uint(y);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const float a = fabsf(y);
+    uint32_t mag;
+    if (a < 0.015625f) {
+        // below 2^-6 the format is a fixed grid of 2^-9 steps; a count of 8
+        // is the smallest normal, whose code is also 8
+        mag = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+    } else {
+        const uint32_t ab = bits & 0x7FFFFFFFu;
+        const uint32_t e = (ab >> 23) - 120u;            // rebias 127 -> 7
+        const uint32_t m = ab & 0x7FFFFFu;
+        mag = (e << 3) | (m >> 20);
+        const uint32_t rem = m & 0xFFFFFu;               // 20 dropped mantissa bits
+        mag += (rem > 0x80000u) | ((rem == 0x80000u) & (mag & 1u));
+    }
+    return sign | mag;
+}
+
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restrict__ x, uint8_t* __restrict__ x8,
+                                                        float* __restrict__ scale, int N, int D, int n_tiles) {
+    __shared__ float red[4];
+    const int tile = blockIdx.x;
+    const int bh = tile / n_tiles, t = tile - bh * n_tiles;
+    const int r0 = 64 * t;
+    const int rows = min(64, N - r0);
+    const int n_chunks = rows * D / 8;                   // 8 bf16 per 16-byte chunk
+    const size_t base = (static_cast<size_t>(bh) * N + r0) * D;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + base);
+
+    float amax = 0.0f;
+    for (int c = threadIdx.x; c < n_chunks; c += 256) {
+        const u32x4 u = src[c];
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+            amax = fmaxf(amax, fabsf(__uint_as_float(u[wd] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(u[wd] & 0xFFFF0000u)));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = 448.0f / fmaxf(amax, 1e-6f);         // IEEE-rounded fp32 division
+    if (threadIdx.x == 0) scale[tile] = s;
+
+    u32x2* dst = reinterpret_cast<u32x2*>(x8 + base);
+    for (int c = threadIdx.x; c < n_chunks; c += 256) {
+        const u32x4 u = src[c];
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t hb = (e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16);
+            float y = __uint_as_float(hb) * s;
+            y = fminf(fmaxf(y, -448.0f), 448.0f);
+            packed[e >> 2] |= e4m3_code(y) << (8 * (e & 3));
+        }
+        dst[c] = u32x2{packed[0], packed[1]};
+    }
+}
+
+template <int D, bool CAUSAL, bool FP8>
+hipError_t launch_bf(const KParams& kp, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, FP8>), dim3(grid), dim3(256), 0, st, kp);
+    return hipGetLastError();
+}
+template <int D, bool CAUSAL>
+hipError_t launch_f32(const KParams& kp, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, st, kp);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_d(const FwdArgs& a, const KParams& kp, int grid, hipStream_t st) {
+    switch (a.kind) {
+        case Kind::F32:
+            return a.causal ? launch_f32<D, true>(kp, grid, st) : launch_f32<D, false>(kp, grid, st);
+        case Kind::BF16:
+            return a.causal ? launch_bf<D, true, false>(kp, grid, st) : launch_bf<D, false, false>(kp, grid, st);
+        case Kind::FP8:
+            return a.causal ? launch_bf<D, true, true>(kp, grid, st) : launch_bf<D, false, true>(kp, grid, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+    KParams kp;
+    kp.q = static_cast<const uint8_t*>(a.q);
+    kp.k = static_cast<const uint8_t*>(a.k);
+    kp.v = static_cast<const uint8_t*>(a.v);
+    kp.o = static_cast<uint8_t*>(a.o);
+    kp.lse = a.lse;
+    kp.q_scale = a.q_scale;
+    kp.k_scale = a.k_scale;
+    kp.BH = a.BH;
+    kp.N = a.N;
+    kp.n_qtiles = (a.N + 127) / 128;
+    kp.c_log2 = a.softmax_scale * kLog2e;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * a.BH;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    switch (a.d) {
+        case 32: return dispatch_d<32>(a, kp, static_cast<int>(grid), stream);
+        case 64: return dispatch_d<64>(a, kp, static_cast<int>(grid), stream);
+        case 128: return dispatch_d<128>(a, kp, static_cast<int>(grid), stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale, int BH, int N, int d,
+                            hipStream_t stream) {
+    const int n_tiles = (N + 63) / 64;
+    const long long grid = static_cast<long long>(BH) * n_tiles;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<int>(grid)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(x_bf16), x8, scale, N, d, n_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace fa

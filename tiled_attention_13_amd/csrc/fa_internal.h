@@ -1,0 +1,34 @@
+// Internal interface between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum class Kind { F32, BF16, FP8 };
+
+struct FwdArgs {
+    Kind kind;
+    const void* q;          // f32 / bf16 / e4m3 codes
+    const void* k;
+    const void* v;          // f32 or bf16
+    void* o;                // f32 or bf16
+    float* lse;             // may be null
+    const float* q_scale;   // FP8 only: [BH, ceil(N/64)]
+    const float* k_scale;
+    int BH;
+    int N;
+    int d;
+    bool causal;
+    float softmax_scale;
+};
+
+// Enqueue the forward kernel on `stream`; returns the launch status.
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// Enqueue the per-64-row-tile e4m3fn quantisation of a bf16 [BH, N, d] tensor.
+hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale,
+                            int BH, int N, int d, hipStream_t stream);
+
+}  // namespace fa
