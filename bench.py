@@ -64,7 +64,7 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     except Exception:  # threadpoolctl missing or no BLAS info
         threads = 1
     rows_per_chunk = 256
-    stride = max(1, w.N // 1024)
+    stride = max(1, w.N // 4096)
     t0 = time.perf_counter()
     done = 0
     heads = 0

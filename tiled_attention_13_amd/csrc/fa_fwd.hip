@@ -90,18 +90,29 @@ __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 *
 // ---------------------------------------------------------------------------
 // Online-softmax step on the scores one lane holds for its query.
 // s[NS]: scores (already masked to -inf), c: scale into base-2 units.
-// Updates m (base-2 running max) and l (this lane's part of the running sum),
-// overwrites s with the probabilities and returns the rescale factor alpha.
+// Updates m (base-2 reference max) and l (this lane's part of the running
+// sum), overwrites s with the probabilities and returns the factor alpha by
+// which the partial O must be rescaled.
+//
+// The reference max only moves when the tile's max exceeds it by more than
+// kRescaleSlack (base-2 units).  Softmax is invariant to the reference, so
+// the result is the same; probabilities are then bounded by 2^kRescaleSlack
+// instead of 1 (harmless in fp32 and bf16), and most tiles need no rescale.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleSlack = 8.0f;
+
 template <int NS>
 __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m, float& l) {
     float mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < NS; ++i) mx = fmaxf(mx, s[i]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == kNegInf) ? 0.0f : m_new;   // nothing unmasked yet
-    const float alpha = fast_exp2(m - m_use);
+    const float mx2 = max_halves(mx) * c;
+    float alpha = 1.0f;
+    if (mx2 > m + kRescaleSlack) {        // also taken on the first unmasked tile (m = -inf)
+        alpha = fast_exp2(m - mx2);
+        m = mx2;
+    }
+    const float m_use = (m == kNegInf) ? 0.0f : m;   // nothing unmasked yet: all p are 0
     float rs = 0.0f;
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -110,7 +121,6 @@ __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m,
         rs += p;
     }
     l = fmaf(l, alpha, rs);
-    m = m_new;
     return alpha;
 }
 
@@ -205,14 +215,34 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(KParams p) {
     u32x4 vst[C::V_PER_T][4];
     auto load_tile = [&](int j) {
         const int n0 = j * BN;
+        const uint8_t* kt = kg + static_cast<size_t>(n0) * D * QK_ES;
+        const uint8_t* vt = vg + static_cast<size_t>(n0) * D * 2;
+        if (n0 + BN <= N) {                        // full tile: no per-row guards
+#pragma unroll
+            for (int i = 0; i < C::K_PER_T; ++i) {
+                const int c = i * 256 + tid;
+                if (c < C::K_CHUNKS) {
+                    const int row = c / C::K_CPR, col = c - row * C::K_CPR;
+                    kst[i] = ld16(kt + row * D * QK_ES + 16 * col);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < C::V_PER_T; ++i) {
+                const int u = i * 256 + tid;
+                if (u < C::V_UNITS) {
+                    const int kq = u % (BN / 4), dg = u / (BN / 4);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) vst[i][r] = ld16(vt + 2 * ((4 * kq + r) * D + 8 * dg));
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < C::K_PER_T; ++i) {
             const int c = i * 256 + tid;
             if (c < C::K_CHUNKS) {
                 const int row = c / C::K_CPR, col = c - row * C::K_CPR;
-                const int key = n0 + row;
-                kst[i] = key < N ? ld16(kg + (static_cast<size_t>(key) * D) * QK_ES + 16 * col)
-                                 : u32x4{0, 0, 0, 0};
+                kst[i] = n0 + row < N ? ld16(kt + row * D * QK_ES + 16 * col) : u32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -221,11 +251,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(KParams p) {
             if (u < C::V_UNITS) {
                 const int kq = u % (BN / 4), dg = u / (BN / 4);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = n0 + 4 * kq + r;
-                    vst[i][r] = key < N ? ld16(vg + 2 * (static_cast<size_t>(key) * D + 8 * dg))
-                                        : u32x4{0, 0, 0, 0};
-                }
+                for (int r = 0; r < 4; ++r)
+                    vst[i][r] = n0 + 4 * kq + r < N ? ld16(vt + 2 * ((4 * kq + r) * D + 8 * dg))
+                                                    : u32x4{0, 0, 0, 0};
             }
         }
     };
