@@ -1,37 +1,38 @@
 // Fused attention forward for gfx950 (MI355X): O = softmax(scale * Q K^T) V and lse.
 //
-// One workgroup owns a tile of BM = 128 queries of one (batch, head) and
-// walks the key/value sequence in tiles of BN keys, the tiled double loop of
-// "Core principles behind FlashAttention's speed-up" (section 1.1) in the
-// FlashAttention-2 order (parallel over batch, heads and query tiles; the
+// A workgroup owns a tile of queries of one (batch, head) and walks the
+// key/value sequence in 64-key tiles: the tiled double loop of "Core
+// principles behind FlashAttention's speed-up" (section 1.1) in the
+// FlashAttention-2 order, parallel over batch, heads and query tiles (the
 // "Flash Attention" tag page, excerpt on V2).  Everything between loading a
 // K/V tile and writing O stays in registers and LDS (same page, section 1.2).
 //
-// Per wave: 32 queries.  Scores are produced transposed, S^T = K Q^T, on
-// 32x32 MFMAs: A = 32 keys from LDS, B = 32 queries held in registers for
-// the whole loop.  In the 32x32 accumulator layout lane l owns column
-// l % 32, so every lane holds 16 scores of ONE query (the other 16 of each
-// 32-key block sit in lane l ^ 32).  Row reductions are therefore in-lane
-// plus one v_permlane32_swap, and the probabilities already sit where the
-// B operand of the next MFMA, O^T += V^T P^T, wants them: no LDS round trip
-// for P.  V^T is produced while K/V tiles are copied into LDS.
+// Scores are produced transposed, S^T = K Q^T, on 32x32 MFMAs: A = 32 keys
+// from LDS, B = 32 queries held in registers for the whole loop.  In the
+// 32x32 accumulator layout lane l owns column l % 32, so every lane holds 16
+// scores of ONE query (the other 16 of each 32-key block sit in lane l ^ 32).
+// Row reductions are in-lane plus one v_permlane32_swap, and the
+// probabilities already sit where the B operand of O^T += V^T P^T wants
+// them: P never goes through LDS.  V^T is produced while tiles are copied
+// into LDS.
 //
 // Online softmax (Triton walkthrough page, section 2.1): running max m and
 // running sum l per query, kept in base-2 units with softmax_scale*log2(e)
 // folded into one FMA before v_exp_f32; the accumulator is rescaled by
-// exp2(m_old - m_new) (skipped when that factor is 1 in every lane), and
-// the division by l is deferred to the epilogue (tag page, excerpt on V2).
-// l is summed from the fp32 probabilities before they are rounded to bf16.
+// exp2(m_old - m_new) and the division by l is deferred to the epilogue (tag
+// page, excerpt on V2).  l is summed from the fp32 probabilities before they
+// are rounded to bf16.
 //
 // Causal (Triton walkthrough page, section 3.1): key tiles entirely above
-// the diagonal are never loaded, a wave skips tiles that lie above its own
-// rows, and only tiles that cross the diagonal or the sequence end compare
+// the diagonal are never loaded, a wave skips tiles above its own rows, and
+// only the tile that crosses the diagonal (or the sequence end) compares
 // indices.  Workgroups are issued heaviest query tile first.
 //
 // FP8 (same page, section 4.1): Q and K arrive as e4m3fn codes with one
-// fp32 scale per 64-row tile; S^T runs on the 32x32x64 f8f6f4 MFMA and the
-// dequantisation 1/(q_scale*k_scale) is folded into the exp2 constant
-// (BN = 64 keeps one K scale per tile).  V and P*V stay bf16.
+// fp32 scale per 64-row tile; S^T runs on the 32x32x64 f8f6f4 MFMA (32x32x16
+// fp8 for d = 32) and the dequantisation 1/(q_scale*k_scale) is folded into
+// the exp2 constant (64-key tiles keep one K scale per tile).  V and P*V stay
+// bf16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -124,31 +125,6 @@ __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m,
     return alpha;
 }
 
-// ===========================================================================
-// bf16 / fp8 kernel
-// ===========================================================================
-template <int D, bool CAUSAL, bool FP8>
-struct Cfg {
-    static constexpr int NW = 4;                 // waves per workgroup
-    static constexpr int BM = 32 * NW;           // queries per workgroup
-    static constexpr int BN = 64;                // keys per tile
-    static constexpr int KROW = FP8 ? D + 16 : 2 * D + 16;   // bytes per K row in LDS (padded)
-    static constexpr int VROW = 2 * BN + 16;     // bytes per V^T row in LDS (padded)
-    static constexpr int KBYTES = BN * KROW;
-    static constexpr int VBYTES = D * VROW;
-    static constexpr int STAGE = KBYTES + VBYTES;
-    static constexpr int K_CHUNKS = BN * (FP8 ? D : 2 * D) / 16;   // 16-byte chunks per K tile
-    static constexpr int K_CPR = (FP8 ? D : 2 * D) / 16;           // chunks per K row
-    static constexpr int K_PER_T = (K_CHUNKS + 255) / 256;
-    static constexpr int V_UNITS = (BN / 4) * (D / 8);             // 4 keys x 8 dims each
-    static constexpr int V_PER_T = (V_UNITS + 255) / 256;
-    // FP8 with D a multiple of 64 uses the 32x32x64 f8f6f4 MFMA (32 codes per
-    // lane); D = 32 uses the 32x32x16 fp8 MFMA (8 codes per lane).
-    static constexpr bool F8W = FP8 && (D % 64 == 0);
-    static constexpr bool F8N = FP8 && !F8W;
-    static constexpr int QREGS = F8W ? D / 64 : D / 16;            // k steps of S^T
-};
-
 // LDS column of key `kk` (0..63) inside a V^T row.  Keys are permuted within
 // each group of 16 so that the eight keys one lane contracts over in a P*V
 // MFMA are adjacent (one 16-byte read); see the P fragment layout below.
@@ -157,112 +133,177 @@ __device__ __forceinline__ int vt_slot(int kk) {
     return 16 * c + 8 * hh + 4 * a + b;
 }
 
+// ===========================================================================
+// bf16 / fp8 kernel, ping-pong schedule
+//
+// 8 waves, 256 queries per workgroup (32 per wave), 64-key tiles shared by all
+// eight waves through a 3-stage LDS ring.  Waves 0-3 (group A) and 4-7
+// (group B) sit one per SIMD each and run half a tile apart: every barrier
+// ends a "slot" in which one group issues the matrix-core work of a tile
+// (O^T += V^T P^T for the previous tile, then S^T = K Q^T for this one) while
+// the other runs the softmax, rescale and tile copy on the vector ALUs, so
+// each SIMD always has MFMA work from one wave to overlap the other's VALU.
+//
+// Per wave the op sequence is M_0 V_0 M_1 V_1 ... V_{n-1} M_n with
+//   M_j = { PV_{j-1}, S_j }   (matrix cores)
+//   V_j = { softmax_j, rescale, publish a staged tile, prefetch the next }
+// group A runs op k in slot k, group B in slot k+1.  Tile t lives in LDS
+// buffer t % 3.  A writes its half of tile t in V_{t-1} (slot 2t-1), B in
+// V_{t-2} (slot 2t-2); the last reader of the previous occupant (B's PV in
+// slot 2t-3) is done by then, and A first reads tile t in slot 2t.  Global
+// loads land in registers two slots before they are written to LDS.
+// ===========================================================================
 template <int D, bool CAUSAL, bool FP8>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(KParams p) {
-    using C = Cfg<D, CAUSAL, FP8>;
-    constexpr int BM = C::BM, BN = C::BN;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+struct PPCfg {
+    static constexpr int NW = 8;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BM = 32 * NW;           // queries per workgroup
+    static constexpr int BN = 64;                // keys per tile
+    static constexpr int STAGES = 3;
+    static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
+    static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
+    static constexpr int VROW = 2 * BN + 16;     // bytes per V^T row in LDS (padded)
+    static constexpr int KBYTES = BN * KROW;
+    static constexpr int VBYTES = D * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int K_CPR = D * ES / 16;    // 16-byte chunks per K row
+    static constexpr int K_CHUNKS = BN * K_CPR;
+    static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
+    static constexpr int V_UNITS = (BN / 2) * (D / 8);   // 2 keys x 8 dims each
+    static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+    static constexpr bool F8W = FP8 && (D % 64 == 0);
+    static constexpr bool F8N = FP8 && !F8W;
+    static constexpr int QREGS = F8W ? D / 64 : D / 16;
+};
+
+// Scheduling pattern for a block of N (16-byte LDS read -> MFMA) pairs: issue
+// AHEAD reads first, then alternate one MFMA with one further read, so each
+// MFMA's operand was requested about AHEAD MFMAs (~32 cycles each) earlier.
+constexpr int kLdsAhead = 6;
+template <int N, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+    constexpr int A = AHEAD < N ? AHEAD : N;
+    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
+// Barrier that orders LDS traffic only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+template <int D, bool CAUSAL, bool FP8>
+__global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
+    using C = PPCfg<D, CAUSAL, FP8>;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT, ES = C::ES;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    // wave index as a scalar, so every per-wave decision below is a uniform branch
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, grp = w >> 2, h = lane >> 5, l32 = lane & 31;
     const int N = p.N;
 
     int qt = blockIdx.x / p.BH;
     const int bh = blockIdx.x - qt * p.BH;
     if (CAUSAL) qt = p.n_qtiles - 1 - qt;        // heaviest query tiles first
     const int q0 = qt * BM;
-    const int qw0 = q0 + 32 * w;                  // this wave's first query
+    const int qw0 = q0 + 32 * w;
     const int my_q = qw0 + l32;
 
-    const size_t slice = static_cast<size_t>(bh) * N * D;     // elements before this (b, h)
-    constexpr int QK_ES = FP8 ? 1 : 2;                         // bytes per Q/K element
-    const uint8_t* qg = p.q + slice * QK_ES;
-    const uint8_t* kg = p.k + slice * QK_ES;
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* qg = p.q + slice * ES;
+    const uint8_t* kg = p.k + slice * ES;
     const uint8_t* vg = p.v + slice * 2;
 
-    // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop
+    // ---- Q fragments (B operand of S^T = K Q^T)
     u32x4 qf[C::F8W ? 2 * C::QREGS : C::QREGS];
     {
         const bool ok = my_q < N;
-        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * QK_ES;
+        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * ES;
 #pragma unroll
         for (int i = 0; i < C::QREGS; ++i) {
             if constexpr (C::F8W) {
-                // 32 codes per lane per 64-wide k step: dims 64i + 32h .. +31
                 qf[2 * i] = ok ? ld16(row + 64 * i + 32 * h) : u32x4{0, 0, 0, 0};
                 qf[2 * i + 1] = ok ? ld16(row + 64 * i + 32 * h + 16) : u32x4{0, 0, 0, 0};
             } else if constexpr (C::F8N) {
-                // 8 codes per lane per 16-wide k step: dims 16i + 8h .. +7
                 const u32x2 x = ok ? *reinterpret_cast<const u32x2*>(row + 16 * i + 8 * h) : u32x2{0, 0};
                 qf[i] = u32x4{x[0], x[1], 0, 0};
             } else {
-                // 8 bf16 per lane per 16-wide k step: dims 16i + 8h .. +7
                 qf[i] = ok ? ld16(row + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
             }
         }
     }
 
-    const int n_ktiles_all = (N + BN - 1) / BN;
-    const int n_scale = (N + 63) / 64;            // FP8 scales per (b, h): one per 64 rows
+    const int n_scale = (N + 63) / 64;
     float c_q = p.c_log2;
     if (FP8) c_q = p.c_log2 / p.q_scale[bh * n_scale + (qw0 < N ? qw0 : N - 1) / 64];
 
-    const int q_end = min(q0 + BM, N);
-    const int n_kt = CAUSAL ? min(n_ktiles_all, (q_end + BN - 1) / BN) : n_ktiles_all;
+    const int n_all = (N + BN - 1) / BN;
+    const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
+    // last key tile with any key at or before this wave's last query
+    const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
 
-    // ---- global -> register staging of one K/V tile
+    // ---- global -> register staging of this thread's share of one K/V tile
     u32x4 kst[C::K_PER_T];
-    u32x4 vst[C::V_PER_T][4];
-    auto load_tile = [&](int j) {
-        const int n0 = j * BN;
-        const uint8_t* kt = kg + static_cast<size_t>(n0) * D * QK_ES;
+    u32x4 vst[C::V_PER_T][2];
+    auto load_tile = [&](int t) {
+        const int n0 = t * BN;
+        const uint8_t* kt = kg + static_cast<size_t>(n0) * D * ES;
         const uint8_t* vt = vg + static_cast<size_t>(n0) * D * 2;
         if (n0 + BN <= N) {                        // full tile: no per-row guards
 #pragma unroll
             for (int i = 0; i < C::K_PER_T; ++i) {
-                const int c = i * 256 + tid;
+                const int c = i * NT + tid;
                 if (c < C::K_CHUNKS) {
                     const int row = c / C::K_CPR, col = c - row * C::K_CPR;
-                    kst[i] = ld16(kt + row * D * QK_ES + 16 * col);
+                    kst[i] = ld16(kt + row * D * ES + 16 * col);
                 }
             }
 #pragma unroll
             for (int i = 0; i < C::V_PER_T; ++i) {
-                const int u = i * 256 + tid;
+                const int u = i * NT + tid;
                 if (u < C::V_UNITS) {
-                    const int kq = u % (BN / 4), dg = u / (BN / 4);
+                    const int kp = u % (BN / 2), dg = u / (BN / 2);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) vst[i][r] = ld16(vt + 2 * ((4 * kq + r) * D + 8 * dg));
+                    for (int r = 0; r < 2; ++r) vst[i][r] = ld16(vt + 2 * ((2 * kp + r) * D + 8 * dg));
                 }
             }
             return;
         }
 #pragma unroll
         for (int i = 0; i < C::K_PER_T; ++i) {
-            const int c = i * 256 + tid;
+            const int c = i * NT + tid;
             if (c < C::K_CHUNKS) {
                 const int row = c / C::K_CPR, col = c - row * C::K_CPR;
-                kst[i] = n0 + row < N ? ld16(kt + row * D * QK_ES + 16 * col) : u32x4{0, 0, 0, 0};
+                kst[i] = n0 + row < N ? ld16(kt + row * D * ES + 16 * col) : u32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
         for (int i = 0; i < C::V_PER_T; ++i) {
-            const int u = i * 256 + tid;
+            const int u = i * NT + tid;
             if (u < C::V_UNITS) {
-                const int kq = u % (BN / 4), dg = u / (BN / 4);
+                const int kp = u % (BN / 2), dg = u / (BN / 2);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    vst[i][r] = n0 + 4 * kq + r < N ? ld16(vt + 2 * ((4 * kq + r) * D + 8 * dg))
-                                                    : u32x4{0, 0, 0, 0};
+                for (int r = 0; r < 2; ++r)
+                    vst[i][r] = n0 + 2 * kp + r < N ? ld16(vt + 2 * ((2 * kp + r) * D + 8 * dg))
+                                                   : u32x4{0, 0, 0, 0};
             }
         }
     };
-    auto store_tile = [&](int buf) {
-        uint8_t* ks = smem + buf * C::STAGE;
+    auto store_tile = [&](int t) {
+        uint8_t* ks = smem + (t % C::STAGES) * C::STAGE;
         uint8_t* vs = ks + C::KBYTES;
 #pragma unroll
         for (int i = 0; i < C::K_PER_T; ++i) {
-            const int c = i * 256 + tid;
+            const int c = i * NT + tid;
             if (c < C::K_CHUNKS) {
                 const int row = c / C::K_CPR, col = c - row * C::K_CPR;
                 *reinterpret_cast<u32x4*>(ks + row * C::KROW + 16 * col) = kst[i];
@@ -270,132 +311,180 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(KParams p) {
         }
 #pragma unroll
         for (int i = 0; i < C::V_PER_T; ++i) {
-            const int u = i * 256 + tid;
+            const int u = i * NT + tid;
             if (u < C::V_UNITS) {
-                const int kq = u % (BN / 4), dg = u / (BN / 4);
-                uint8_t* dst = vs + 2 * vt_slot(4 * kq);
+                const int kp = u % (BN / 2), dg = u / (BN / 2);
+                uint8_t* dst = vs + 2 * vt_slot(2 * kp);          // keys 2kp, 2kp+1 stay adjacent
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    // dim 8*dg+e of keys 4kq..4kq+3 -> 8 contiguous bytes of V^T
                     const int wd = e >> 1, sh = 16 * (e & 1);
                     const uint32_t x0 = (vst[i][0][wd] >> sh) & 0xFFFFu;
                     const uint32_t x1 = (vst[i][1][wd] >> sh) & 0xFFFFu;
-                    const uint32_t x2 = (vst[i][2][wd] >> sh) & 0xFFFFu;
-                    const uint32_t x3 = (vst[i][3][wd] >> sh) & 0xFFFFu;
-                    *reinterpret_cast<u32x2*>(dst + (8 * dg + e) * C::VROW) =
-                        u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+                    *reinterpret_cast<uint32_t*>(dst + (8 * dg + e) * C::VROW) = x0 | (x1 << 16);
                 }
             }
         }
     };
 
-    // ---- accumulators: O^T, lane owns query l32, dims acc_row(v, h) of each 32-dim block
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
     float m_run = kNegInf, l_run = 0.0f;
+    float s[BN / 2];
+    bf16x8 pf[BN / 16];
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int j = 0; j < n_kt; ++j) {
-        const int n0 = j * BN;
-        const bool more = j + 1 < n_kt;
-        if (more) load_tile(j + 1);
-
-        const bool active = !CAUSAL || n0 <= qw0 + 31;     // wave-uniform
-        if (active) {
-            const uint8_t* ks = smem + (j & 1) * C::STAGE;
-            const uint8_t* vs = ks + C::KBYTES;
-
-            // S^T for BN keys: s[kb] holds keys n0 + 32kb + acc_row(v, h)
-            f32x16 sacc[BN / 32];
+    // ---- the four ops of the schedule
+    // S^T = K_j Q^T for tile j
+    auto op_s = [&](int j) {
+        const uint8_t* ks = smem + (j % C::STAGES) * C::STAGE;
+        if constexpr (!FP8) {
+            // bf16: all K fragments first, MFMAs of the two 32-key blocks interleaved
+            constexpr int NA = (BN / 32) * C::QREGS;
+            bf16x8 a[NA];
 #pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) {
-                f32x16 acc;
+            for (int i = 0; i < C::QREGS; ++i)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-                const uint8_t* krow = ks + (32 * kb + l32) * C::KROW;
+                for (int kb = 0; kb < BN / 32; ++kb)
+                    a[i * (BN / 32) + kb] =
+                        __builtin_bit_cast(bf16x8, ld16(ks + (32 * kb + l32) * C::KROW + 2 * (16 * i + 8 * h)));
+            f32x16 acc[BN / 32];
 #pragma unroll
-                for (int i = 0; i < C::QREGS; ++i) {
-                    if constexpr (C::F8W) {
-                        const u32x4 a0 = ld16(krow + 64 * i + 32 * h);
-                        const u32x4 a1 = ld16(krow + 64 * i + 32 * h + 16);
-                        const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                                         (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-                        const u32x4 b0 = qf[2 * i], b1 = qf[2 * i + 1];
-                        const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
-                                         (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-                        // fp8 e4m3 x fp8 e4m3, unit block scales (E8M0 127 = 2^0)
-                        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
-                    } else if constexpr (C::F8N) {
-                        const long a = __builtin_bit_cast(long, *reinterpret_cast<const u32x2*>(krow + 16 * i + 8 * h));
-                        const long b = __builtin_bit_cast(long, u32x2{qf[i][0], qf[i][1]});
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, acc, 0, 0, 0);
-                    } else {
-                        const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(krow + 2 * (16 * i + 8 * h)));
-                        const bf16x8 b = __builtin_bit_cast(bf16x8, qf[i]);
-                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-                    }
-                }
-                sacc[kb] = acc;
-            }
-
-            float s[BN / 2];
+            for (int kb = 0; kb < BN / 32; ++kb) acc[kb] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)
+                    acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i * (BN / 32) + kb],
+                                                                     __builtin_bit_cast(bf16x8, qf[i]), acc[kb], 0, 0, 0);
+            pipeline_lds_mfma<NA, kLdsAhead>();
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) s[16 * kb + v] = sacc[kb][v];
-
-            const bool need_mask = (CAUSAL && n0 + BN - 1 > qw0) || (n0 + BN > N);
-            if (need_mask) {
+                for (int v = 0; v < 16; ++v) s[16 * kb + v] = acc[kb][v];
+            return;
+        }
 #pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb)
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            f32x16 acc = {};
+            const uint8_t* krow = ks + (32 * kb + l32) * C::KROW;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int key = n0 + 32 * kb + acc_row(v, h);
-                        if (key >= N || (CAUSAL && key > my_q)) s[16 * kb + v] = kNegInf;
-                    }
-            }
-
-            float c = c_q;
-            if (FP8) c = c_q / p.k_scale[bh * n_scale + j];     // BN = 64: tile j is scale tile j
-
-            const float alpha = softmax_step(s, c, m_run, l_run);
-            if (!__all(alpha == 1.0f)) {
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-            }
-
-            // P fragments (B operand of O^T += V^T P^T) for 16-key step c:
-            // slot t of lane (l32, h) <- s[8c + t], i.e. key 16c + 8(t/4) + 4h + t%4.
-            bf16x8 pf[BN / 16];
-#pragma unroll
-            for (int cc = 0; cc < BN / 16; ++cc)
-#pragma unroll
-                for (int t = 0; t < 8; ++t) pf[cc][t] = static_cast<__bf16>(s[8 * cc + t]);
-
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const uint8_t* vrow = vs + (32 * db + l32) * C::VROW;
-#pragma unroll
-                for (int cc = 0; cc < BN / 16; ++cc) {
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(vrow + 2 * (16 * cc + 8 * h)));
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[cc], o[db], 0, 0, 0);
+            for (int i = 0; i < C::QREGS; ++i) {
+                if constexpr (C::F8W) {
+                    const u32x4 a0 = ld16(krow + 64 * i + 32 * h);
+                    const u32x4 a1 = ld16(krow + 64 * i + 32 * h + 16);
+                    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    const u32x4 b0 = qf[2 * i], b1 = qf[2 * i + 1];
+                    const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
+                                     (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+                    // fp8 e4m3 x fp8 e4m3, unit block scales (E8M0 127 = 2^0)
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+                } else if constexpr (C::F8N) {
+                    const long a = __builtin_bit_cast(long, *reinterpret_cast<const u32x2*>(krow + 16 * i + 8 * h));
+                    const long b = __builtin_bit_cast(long, u32x2{qf[i][0], qf[i][1]});
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(a, b, acc, 0, 0, 0);
+                } else {
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, ld16(krow + 2 * (16 * i + 8 * h)));
+                    const bf16x8 b = __builtin_bit_cast(bf16x8, qf[i]);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
                 }
             }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[16 * kb + v] = acc[v];
         }
+    };
+    // O^T += V_j^T P^T for tile j
+    auto op_pv = [&](int j) {
+        const uint8_t* vs = smem + (j % C::STAGES) * C::STAGE + C::KBYTES;
+        constexpr int NA = (D / 32) * (BN / 16);
+        bf16x8 a[NA];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc)
+                a[db * (BN / 16) + cc] =
+                    __builtin_bit_cast(bf16x8, ld16(vs + (32 * db + l32) * C::VROW + 2 * (16 * cc + 8 * h)));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db * (BN / 16) + cc], pf[cc], o[db], 0, 0, 0);
+        pipeline_lds_mfma<NA, kLdsAhead>();
+    };
+    // softmax of tile j, rescale of O, probabilities packed to bf16
+    auto op_softmax = [&](int j, bool masked) {
+        const int n0 = j * BN;
+        if (masked) {
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = n0 + 32 * kb + acc_row(v, h);
+                    if (key >= N || (CAUSAL && key > my_q)) s[16 * kb + v] = kNegInf;
+                }
+        }
+        float c = c_q;
+        if (FP8) c = c_q / p.k_scale[bh * n_scale + j];     // BN = 64: tile j is scale tile j
+        const float alpha = softmax_step(s, c, m_run, l_run);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < BN / 16; ++cc)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) pf[cc][t] = static_cast<__bf16>(s[8 * cc + t]);
+    };
+    // this wave's share of the tile traffic in V_j: publish tile j+lead, prefetch tile j+lead+1
+    const int lead = grp == 0 ? 1 : 2;
+    auto traffic = [&](int j) {
+        const int ts = j + lead;
+        if (ts < n_kt) store_tile(ts);
+        if (ts + 1 < n_kt) load_tile(ts + 1);
+    };
 
-        if (more) store_tile((j + 1) & 1);
-        __syncthreads();
+    // ---- prologue: group A publishes its half of tile 0, group B of tiles 0 and 1
+    for (int t = 0; t < lead && t < n_kt; ++t) {
+        load_tile(t);
+        store_tile(t);
     }
+    if (lead < n_kt) load_tile(lead);
+    lds_barrier();
+    if (grp == 1) lds_barrier();                  // group B idles through slot 0
 
-    // ---- epilogue: O = O^T / l, lse = ln2 * (m + log2 l)
+    // ---- slots.  Barrier k (k = 1, 2, ...) of this wave ends its op k-1:
+    //      M_0 | V_0 M_1 | V_1 M_2 | ... | V_{n-1} M_n
+    // Tiles before j_last need no mask (their last key precedes this wave's
+    // first query, and only the last tile can hold keys >= N).
+    op_s(0);
+    lds_barrier();
+    for (int j = 0; j < j_last; ++j) {
+        op_softmax(j, false);
+        traffic(j);
+        lds_barrier();
+        op_pv(j);
+        __builtin_amdgcn_sched_barrier(0);
+        op_s(j + 1);
+        lds_barrier();
+    }
+    {
+        const int n0 = j_last * BN;
+        op_softmax(j_last, (CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N);
+        traffic(j_last);
+        lds_barrier();
+        op_pv(j_last);
+        lds_barrier();
+    }
+    for (int j = j_last + 1; j < n_kt; ++j) {     // this wave is past the diagonal: traffic only
+        traffic(j);
+        lds_barrier();
+        lds_barrier();
+    }
+    if (grp == 0) lds_barrier();                  // group A idles through the last slot
+
+    // ---- epilogue
     const float l_tot = sum_halves(l_run);
     if (my_q < N) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
@@ -618,25 +707,33 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
 }
 
 template <int D, bool CAUSAL, bool FP8>
-hipError_t launch_bf(const KParams& kp, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, FP8>), dim3(grid), dim3(256), 0, st, kp);
+hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
+    kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8>), dim3(static_cast<int>(grid)), dim3(PPCfg<D, CAUSAL, FP8>::NT),
+                       0, st, kp);
     return hipGetLastError();
 }
 template <int D, bool CAUSAL>
-hipError_t launch_f32(const KParams& kp, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(256), 0, st, kp);
+hipError_t launch_f32(KParams kp, int BH, hipStream_t st) {
+    kp.n_qtiles = (kp.N + 127) / 128;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(static_cast<int>(grid)), dim3(256), 0, st, kp);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t dispatch_d(const FwdArgs& a, const KParams& kp, int grid, hipStream_t st) {
+hipError_t dispatch_d(const FwdArgs& a, const KParams& kp, hipStream_t st) {
+    const int BH = a.BH;
     switch (a.kind) {
         case Kind::F32:
-            return a.causal ? launch_f32<D, true>(kp, grid, st) : launch_f32<D, false>(kp, grid, st);
+            return a.causal ? launch_f32<D, true>(kp, BH, st) : launch_f32<D, false>(kp, BH, st);
         case Kind::BF16:
-            return a.causal ? launch_bf<D, true, false>(kp, grid, st) : launch_bf<D, false, false>(kp, grid, st);
+            return a.causal ? launch_bf<D, true, false>(kp, BH, st) : launch_bf<D, false, false>(kp, BH, st);
         case Kind::FP8:
-            return a.causal ? launch_bf<D, true, true>(kp, grid, st) : launch_bf<D, false, true>(kp, grid, st);
+            return a.causal ? launch_bf<D, true, true>(kp, BH, st) : launch_bf<D, false, true>(kp, BH, st);
     }
     return hipErrorInvalidValue;
 }
@@ -654,14 +751,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.k_scale = a.k_scale;
     kp.BH = a.BH;
     kp.N = a.N;
-    kp.n_qtiles = (a.N + 127) / 128;
+    kp.n_qtiles = 0;                       // set per kernel from its query-tile height
     kp.c_log2 = a.softmax_scale * kLog2e;
-    const long long grid = static_cast<long long>(kp.n_qtiles) * a.BH;
-    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     switch (a.d) {
-        case 32: return dispatch_d<32>(a, kp, static_cast<int>(grid), stream);
-        case 64: return dispatch_d<64>(a, kp, static_cast<int>(grid), stream);
-        case 128: return dispatch_d<128>(a, kp, static_cast<int>(grid), stream);
+        case 32: return dispatch_d<32>(a, kp, stream);
+        case 64: return dispatch_d<64>(a, kp, stream);
+        case 128: return dispatch_d<128>(a, kp, stream);
     }
     return hipErrorInvalidValue;
 }
