@@ -189,7 +189,7 @@ def main():
         "hbm_gbps_compulsory": round(w.compulsory_bytes() / (kern_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "fa_fwd (fwd_kernel<128, causal, bf16>)",
+                     "kernel": "fwd_pp_kernel<d=128, causal, bf16> (one launch per fa_fwd call)",
                      "per_launch_flops": flops},
         "input_sha256": digest(q, k, v)[:16],
         "input_gen_s": round(gen_s, 2),
