@@ -60,6 +60,11 @@ fa_status launch_status(hipError_t e) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+int padded_keys(int n) { return (n + fa::kKeyTile - 1) / fa::kKeyTile * fa::kKeyTile; }
+
+// bytes of the V^T workspace of the bf16/FP8 kernel: [BH, d, N rounded up to a key tile] bf16
+size_t vt_bytes(int BH, int n, int d) { return static_cast<size_t>(BH) * d * padded_keys(n) * 2; }
+
 }  // namespace
 
 extern "C" {
@@ -108,9 +113,22 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
         !aligned(q_scale, 4) || !aligned(k_scale, 4) || (lse && !aligned(lse, 4)))
         return FA_ERR_MISALIGNED;
     if ((st = check_device()) != FA_OK) return st;
-    fa::FwdArgs a{fa::Kind::FP8, q8, k8, v_bf16, o_bf16, lse, q_scale, k_scale,
-                  static_cast<int>(B * H), static_cast<int>(N), static_cast<int>(d), causal == 1, softmax_scale};
-    return launch_status(fa::launch_fwd(a, static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    void* vt = nullptr;
+    if (hipMallocAsync(&vt, vt_bytes(BH, n, dd), s) != hipSuccess || vt == nullptr) {
+        (void)hipGetLastError();
+        return FA_ERR_OUT_OF_MEMORY;
+    }
+    hipError_t e = fa::launch_transpose_v(v_bf16, vt, BH, n, dd, s);
+    if (e == hipSuccess) {
+        fa::FwdArgs a{fa::Kind::FP8, q8, k8, v_bf16, vt, o_bf16, lse, q_scale, k_scale,
+                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+        e = fa::launch_fwd(a, s);
+    }
+    const hipError_t ef = hipFreeAsync(vt, s);
+    if (e != hipSuccess) return launch_status(e);
+    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
@@ -128,34 +146,49 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
-    if (dtype != FA_FP8_E4M3) {
-        fa::FwdArgs a{dtype == FA_F32 ? fa::Kind::F32 : fa::Kind::BF16, q, k, v, o, lse, nullptr, nullptr,
-                      BH, n, dd, causal == 1, softmax_scale};
+    if (dtype == FA_F32) {
+        fa::FwdArgs a{fa::Kind::F32, q, k, v, nullptr, o, lse, nullptr, nullptr, BH, n, n, dd, causal == 1,
+                      softmax_scale};
         return launch_status(fa::launch_fwd(a, s));
     }
 
-    // FP8: stream-ordered workspace for the e4m3 codes of Q and K and their scales
+    // bf16 / FP8: one stream-ordered workspace for V^T and, for FP8, the e4m3
+    // codes of Q and K and their per-tile scales
+    const bool fp8 = dtype == FA_FP8_E4M3;
     const size_t codes = static_cast<size_t>(BH) * n * dd;
     const size_t n_scales = static_cast<size_t>(BH) * ((n + 63) / 64);
-    const size_t off_k8 = round_up(codes, 256);
-    const size_t off_qs = off_k8 + round_up(codes, 256);
-    const size_t off_ks = off_qs + round_up(n_scales * 4, 256);
-    const size_t total = off_ks + round_up(n_scales * 4, 256);
+    const size_t off_vt = 0;
+    const size_t off_q8 = off_vt + round_up(vt_bytes(BH, n, dd), 256);
+    const size_t off_k8 = off_q8 + (fp8 ? round_up(codes, 256) : 0);
+    const size_t off_qs = off_k8 + (fp8 ? round_up(codes, 256) : 0);
+    const size_t off_ks = off_qs + (fp8 ? round_up(n_scales * 4, 256) : 0);
+    const size_t total = off_ks + (fp8 ? round_up(n_scales * 4, 256) : 0);
     void* ws = nullptr;
     if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
         (void)hipGetLastError();
         return FA_ERR_OUT_OF_MEMORY;
     }
     uint8_t* base = static_cast<uint8_t*>(ws);
-    uint8_t* q8 = base;
-    uint8_t* k8 = base + off_k8;
-    float* qs = reinterpret_cast<float*>(base + off_qs);
-    float* ks = reinterpret_cast<float*>(base + off_ks);
-    hipError_t e = fa::launch_quant_fp8(q, q8, qs, BH, n, dd, s);
-    if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, ks, BH, n, dd, s);
-    if (e == hipSuccess) {
-        fa::FwdArgs a{fa::Kind::FP8, q8, k8, v, o, lse, qs, ks, BH, n, dd, causal == 1, softmax_scale};
-        e = fa::launch_fwd(a, s);
+    void* vt = base + off_vt;
+    hipError_t e = fa::launch_transpose_v(v, vt, BH, n, dd, s);
+    if (!fp8) {
+        if (e == hipSuccess) {
+            fa::FwdArgs a{fa::Kind::BF16, q, k, v, vt, o, lse, nullptr, nullptr, BH, n, padded_keys(n), dd,
+                          causal == 1, softmax_scale};
+            e = fa::launch_fwd(a, s);
+        }
+    } else {
+        uint8_t* q8 = base + off_q8;
+        uint8_t* k8 = base + off_k8;
+        float* qs = reinterpret_cast<float*>(base + off_qs);
+        float* ks = reinterpret_cast<float*>(base + off_ks);
+        if (e == hipSuccess) e = fa::launch_quant_fp8(q, q8, qs, BH, n, dd, s);
+        if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, ks, BH, n, dd, s);
+        if (e == hipSuccess) {
+            fa::FwdArgs a{fa::Kind::FP8, q8, k8, v, vt, o, lse, qs, ks, BH, n, padded_keys(n), dd, causal == 1,
+                          softmax_scale};
+            e = fa::launch_fwd(a, s);
+        }
     }
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launch_status(e);

@@ -57,12 +57,14 @@ struct KParams {
     const uint8_t* q;
     const uint8_t* k;
     const uint8_t* v;
+    const uint8_t* vt;      // V^T [BH, D, np] with tile-permuted keys (bf16/FP8 kernel)
     uint8_t* o;
     float* lse;
     const float* q_scale;
     const float* k_scale;
     int BH;
     int N;
+    int np;
     int n_qtiles;
     float c_log2;       // softmax_scale * log2(e)
 };
@@ -158,7 +160,7 @@ struct PPCfg {
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;           // queries per workgroup
-    static constexpr int BN = 64;                // keys per tile
+    static constexpr int BN = kKeyTile;          // keys per tile
     static constexpr int STAGES = 3;
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
@@ -169,8 +171,8 @@ struct PPCfg {
     static constexpr int K_CPR = D * ES / 16;    // 16-byte chunks per K row
     static constexpr int K_CHUNKS = BN * K_CPR;
     static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-    static constexpr int V_UNITS = (BN / 2) * (D / 8);   // 2 keys x 8 dims each
-    static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+    static constexpr int V_CHUNKS = D * (2 * BN / 16);  // 16-byte chunks of a V^T tile (D rows x BN keys)
+    static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
     static constexpr bool F8W = FP8 && (D % 64 == 0);
     static constexpr bool F8N = FP8 && !F8W;
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
@@ -221,7 +223,8 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* qg = p.q + slice * ES;
     const uint8_t* kg = p.k + slice * ES;
-    const uint8_t* vg = p.v + slice * 2;
+    // V^T rows of this (b, h): D rows of np keys
+    const uint8_t* vtg = p.vt + static_cast<size_t>(bh) * D * p.np * 2;
 
     // ---- Q fragments (B operand of S^T = K Q^T)
     u32x4 qf[C::F8W ? 2 * C::QREGS : C::QREGS];
@@ -253,11 +256,11 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
 
     // ---- global -> register staging of this thread's share of one K/V tile
     u32x4 kst[C::K_PER_T];
-    u32x4 vst[C::V_PER_T][2];
+    u32x4 vst[C::V_PER_T];
     auto load_tile = [&](int t) {
         const int n0 = t * BN;
         const uint8_t* kt = kg + static_cast<size_t>(n0) * D * ES;
-        const uint8_t* vt = vg + static_cast<size_t>(n0) * D * 2;
+        const uint8_t* vt = vtg + static_cast<size_t>(n0) * 2;
         if (n0 + BN <= N) {                        // full tile: no per-row guards
 #pragma unroll
             for (int i = 0; i < C::K_PER_T; ++i) {
@@ -267,34 +270,23 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
                     kst[i] = ld16(kt + row * D * ES + 16 * col);
                 }
             }
+        } else {
 #pragma unroll
-            for (int i = 0; i < C::V_PER_T; ++i) {
-                const int u = i * NT + tid;
-                if (u < C::V_UNITS) {
-                    const int kp = u % (BN / 2), dg = u / (BN / 2);
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) vst[i][r] = ld16(vt + 2 * ((2 * kp + r) * D + 8 * dg));
+            for (int i = 0; i < C::K_PER_T; ++i) {
+                const int c = i * NT + tid;
+                if (c < C::K_CHUNKS) {
+                    const int row = c / C::K_CPR, col = c - row * C::K_CPR;
+                    kst[i] = n0 + row < N ? ld16(kt + row * D * ES + 16 * col) : u32x4{0, 0, 0, 0};
                 }
             }
-            return;
         }
-#pragma unroll
-        for (int i = 0; i < C::K_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < C::K_CHUNKS) {
-                const int row = c / C::K_CPR, col = c - row * C::K_CPR;
-                kst[i] = n0 + row < N ? ld16(kt + row * D * ES + 16 * col) : u32x4{0, 0, 0, 0};
-            }
-        }
+        // V^T rows are padded with zeros up to np, so no guard is needed
 #pragma unroll
         for (int i = 0; i < C::V_PER_T; ++i) {
-            const int u = i * NT + tid;
-            if (u < C::V_UNITS) {
-                const int kp = u % (BN / 2), dg = u / (BN / 2);
-#pragma unroll
-                for (int r = 0; r < 2; ++r)
-                    vst[i][r] = n0 + 2 * kp + r < N ? ld16(vt + 2 * ((2 * kp + r) * D + 8 * dg))
-                                                   : u32x4{0, 0, 0, 0};
+            const int c = i * NT + tid;
+            if (c < C::V_CHUNKS) {
+                const int d = c / (2 * BN / 16), col = c - d * (2 * BN / 16);
+                vst[i] = ld16(vt + static_cast<size_t>(d) * p.np * 2 + 16 * col);
             }
         }
     };
@@ -311,17 +303,10 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         }
 #pragma unroll
         for (int i = 0; i < C::V_PER_T; ++i) {
-            const int u = i * NT + tid;
-            if (u < C::V_UNITS) {
-                const int kp = u % (BN / 2), dg = u / (BN / 2);
-                uint8_t* dst = vs + 2 * vt_slot(2 * kp);          // keys 2kp, 2kp+1 stay adjacent
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int wd = e >> 1, sh = 16 * (e & 1);
-                    const uint32_t x0 = (vst[i][0][wd] >> sh) & 0xFFFFu;
-                    const uint32_t x1 = (vst[i][1][wd] >> sh) & 0xFFFFu;
-                    *reinterpret_cast<uint32_t*>(dst + (8 * dg + e) * C::VROW) = x0 | (x1 << 16);
-                }
+            const int c = i * NT + tid;
+            if (c < C::V_CHUNKS) {
+                const int d = c / (2 * BN / 16), col = c - d * (2 * BN / 16);
+                *reinterpret_cast<u32x4*>(vs + d * C::VROW + 16 * col) = vst[i];
             }
         }
     };
@@ -335,20 +320,25 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     float s[BN / 2];
     bf16x8 pf[BN / 16];
 
+    // per-lane LDS addresses of this lane's K row / V^T row fragments in stage 0
+    const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
+    const uint8_t* lane_v = smem + C::KBYTES + l32 * C::VROW + 16 * h;
+
     // ---- the four ops of the schedule
     // S^T = K_j Q^T for tile j
     auto op_s = [&](int j) {
         const uint8_t* ks = smem + (j % C::STAGES) * C::STAGE;
         if constexpr (!FP8) {
-            // bf16: all K fragments first, MFMAs of the two 32-key blocks interleaved
+            // bf16: all K fragments first, MFMAs of the two 32-key blocks interleaved.
+            // One per-lane address per tile; the fragments differ by immediate offsets.
+            const uint8_t* kl = lane_k + (j % C::STAGES) * C::STAGE;
             constexpr int NA = (BN / 32) * C::QREGS;
             bf16x8 a[NA];
 #pragma unroll
             for (int i = 0; i < C::QREGS; ++i)
 #pragma unroll
                 for (int kb = 0; kb < BN / 32; ++kb)
-                    a[i * (BN / 32) + kb] =
-                        __builtin_bit_cast(bf16x8, ld16(ks + (32 * kb + l32) * C::KROW + 2 * (16 * i + 8 * h)));
+                    a[i * (BN / 32) + kb] = __builtin_bit_cast(bf16x8, ld16(kl + 32 * kb * C::KROW + 32 * i));
             f32x16 acc[BN / 32];
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb) acc[kb] = f32x16{};
@@ -397,15 +387,14 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     };
     // O^T += V_j^T P^T for tile j
     auto op_pv = [&](int j) {
-        const uint8_t* vs = smem + (j % C::STAGES) * C::STAGE + C::KBYTES;
+        const uint8_t* vl = lane_v + (j % C::STAGES) * C::STAGE;
         constexpr int NA = (D / 32) * (BN / 16);
         bf16x8 a[NA];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int cc = 0; cc < BN / 16; ++cc)
-                a[db * (BN / 16) + cc] =
-                    __builtin_bit_cast(bf16x8, ld16(vs + (32 * db + l32) * C::VROW + 2 * (16 * cc + 8 * h)));
+                a[db * (BN / 16) + cc] = __builtin_bit_cast(bf16x8, ld16(vl + 32 * db * C::VROW + 32 * cc));
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -639,6 +628,47 @@ __global__ __launch_bounds__(256, 2) void fwd_f32_kernel(KParams p) {
 }
 
 // ===========================================================================
+// V -> V^T for the bf16/FP8 kernel (one workgroup per 64-key tile)
+//
+// P*V needs each lane's eight contracted keys side by side, i.e. V transposed.
+// Producing V^T once per call keeps the attention kernel's tile copies plain
+// coalesced 16-byte loads and stores.  Within each 64-key tile the keys are
+// stored in vt_slot order (the order the P fragments use), and keys >= N are
+// zero so padded tiles contribute nothing.
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const uint8_t* __restrict__ v, uint8_t* __restrict__ vt,
+                                                          int N, int np, int n_tiles) {
+    constexpr int ROW = 2 * D + 16;                // bytes per key row in LDS (padded)
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kKeyTile * ROW];
+    const int bh = blockIdx.x / n_tiles, t = blockIdx.x - bh * n_tiles;
+    const int n0 = kKeyTile * t;
+    const uint8_t* src = v + (static_cast<size_t>(bh) * N + n0) * D * 2;
+    constexpr int IN_CHUNKS = kKeyTile * D / 8;    // 16-byte chunks of the V tile
+    for (int c = threadIdx.x; c < IN_CHUNKS; c += 256) {
+        const int key = c / (D / 8), col = c - key * (D / 8);
+        const u32x4 x = n0 + key < N ? ld16(src + (key * D + 8 * col) * 2) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(tile + key * ROW + 16 * col) = x;
+    }
+    __syncthreads();
+    uint8_t* dst = vt + (static_cast<size_t>(bh) * D * np + n0) * 2;
+    constexpr int OUT_CHUNKS = D * (kKeyTile / 8); // 8 key slots = 16 bytes per chunk
+    for (int c = threadIdx.x; c < OUT_CHUNKS; c += 256) {
+        const int d = c / (kKeyTile / 8), k8 = c - d * (kKeyTile / 8);
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            // vt_slot swaps bits 2 and 3 of the key index, so it is its own inverse
+            const int k0 = vt_slot(8 * k8 + e), k1 = vt_slot(8 * k8 + e + 1);
+            const uint32_t lo = *reinterpret_cast<const uint16_t*>(tile + k0 * ROW + 2 * d);
+            const uint32_t hi = *reinterpret_cast<const uint16_t*>(tile + k1 * ROW + 2 * d);
+            w[e >> 1] = lo | (hi << 16);
+        }
+        *reinterpret_cast<u32x4*>(dst + (static_cast<size_t>(d) * np + 8 * k8) * 2) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+// ===========================================================================
 // Per-64-row-tile e4m3fn quantisation (one workgroup per tile)
 // ===========================================================================
 
@@ -745,6 +775,8 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.q = static_cast<const uint8_t*>(a.q);
     kp.k = static_cast<const uint8_t*>(a.k);
     kp.v = static_cast<const uint8_t*>(a.v);
+    kp.vt = static_cast<const uint8_t*>(a.vt);
+    kp.np = a.np;
     kp.o = static_cast<uint8_t*>(a.o);
     kp.lse = a.lse;
     kp.q_scale = a.q_scale;
@@ -759,6 +791,22 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
         case 128: return dispatch_d<128>(a, kp, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_transpose_v(const void* v, void* vt, int BH, int N, int d, hipStream_t stream) {
+    const int n_tiles = (N + kKeyTile - 1) / kKeyTile;
+    const int np = n_tiles * kKeyTile;
+    const long long grid = static_cast<long long>(BH) * n_tiles;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    const uint8_t* src = static_cast<const uint8_t*>(v);
+    uint8_t* dst = static_cast<uint8_t*>(vt);
+    switch (d) {
+        case 32: hipLaunchKernelGGL(transpose_v_kernel<32>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
+        case 64: hipLaunchKernelGGL(transpose_v_kernel<64>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
+        case 128: hipLaunchKernelGGL(transpose_v_kernel<128>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale, int BH, int N, int d,

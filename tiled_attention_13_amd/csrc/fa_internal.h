@@ -13,12 +13,14 @@ struct FwdArgs {
     const void* q;          // f32 / bf16 / e4m3 codes
     const void* k;
     const void* v;          // f32 or bf16
+    const void* vt;         // bf16/FP8 kernels: V transposed by launch_transpose_v, [BH, d, np]
     void* o;                // f32 or bf16
     float* lse;             // may be null
     const float* q_scale;   // FP8 only: [BH, ceil(N/64)]
     const float* k_scale;
     int BH;
     int N;
+    int np;                 // row length of vt: N rounded up to the 64-key tile
     int d;
     bool causal;
     float softmax_scale;
@@ -26,6 +28,14 @@ struct FwdArgs {
 
 // Enqueue the forward kernel on `stream`; returns the launch status.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+
+// Keys per tile of the bf16/FP8 attention kernel; V^T rows are padded to a multiple of it.
+constexpr int kKeyTile = 64;
+
+// Enqueue the transposition of a bf16 V [BH, N, d] into vt [BH, d, np] (np = N rounded
+// up to kKeyTile, padding zero), keys permuted within each tile into the order the
+// attention kernel's LDS layout uses.  vt must hold BH * d * np bf16 values.
+hipError_t launch_transpose_v(const void* v, void* vt, int BH, int N, int d, hipStream_t stream);
 
 // Enqueue the per-64-row-tile e4m3fn quantisation of a bf16 [BH, N, d] tensor.
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale,
