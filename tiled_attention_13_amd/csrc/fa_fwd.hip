@@ -417,10 +417,14 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         float c = c_q;
         if (FP8) c = c_q / p.k_scale[bh * n_scale + j];     // BN = 64: tile j is scale tile j
         const float alpha = softmax_step(s, c, m_run, l_run);
+        // with the lazy reference max, alpha is 1 for every lane on most tiles:
+        // skip the 16*D/32 multiplies then (a wave-uniform branch)
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+                for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        }
 #pragma unroll
         for (int cc = 0; cc < BN / 16; ++cc)
 #pragma unroll
