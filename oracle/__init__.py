@@ -28,13 +28,18 @@ Modules:
 * ``fp8`` -- the OCP e4m3fn codec and the per-64-row-tile dynamic scaling.
 * ``online`` -- the pages' block-by-block online-softmax recurrences, used
   only to cross-check the two-pass definition.
+* ``backward`` -- dQ, dK, dV of the forward definition for an upstream
+  gradient dO (the chain rule through scores, softmax and the product with
+  V), in full and for sampled query rows or key columns.
 """
 from .attention import attention, attention_fp8, scores_rows
 from .fp8 import decode_e4m3, encode_e4m3, quantize_tiles, E4M3_MAX, TILE_ROWS
 from .online import online_softmax_attention, online_softmax_eager
+from .backward import attention_backward, dq_rows, dkdv_cols
 
 __all__ = [
     "attention", "attention_fp8", "scores_rows",
     "decode_e4m3", "encode_e4m3", "quantize_tiles", "E4M3_MAX", "TILE_ROWS",
     "online_softmax_attention", "online_softmax_eager",
+    "attention_backward", "dq_rows", "dkdv_cols",
 ]
