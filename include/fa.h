@@ -1,7 +1,7 @@
 /*
- * fa.h -- C ABI of the fused attention forward pass for MI355X (gfx950).
+ * fa.h -- C ABI of fused attention (forward and backward) for MI355X (gfx950).
  *
- * The operation is FlashAttention's forward pass:
+ * The main operation is FlashAttention's forward pass:
  *
  *     O   = softmax(softmax_scale * Q K^T  [causally masked]) V
  *     lse = per-row natural log of the softmax denominator, i.e.
@@ -21,6 +21,10 @@
  *   - "Core principles behind FlashAttention's speed-up": section 1.2
  *     (one fused kernel), 1.3 (online renormalisation), 4.2
  *     (softmax_scale, conventionally 1/sqrt(dim)).
+ *
+ * fa_bwd is its gradient: dQ, dK, dV for an upstream gradient dO, with the
+ * probabilities recomputed from Q, K and the forward's lse instead of stored
+ * (Triton walkthrough page, section 2.2).
  *
  * Conventions shared by every entry point
  *   - Tensors are dense, contiguous, row-major [B, H, N, d] (batch, heads,
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
     FA_F32 = 0,       /* q, k, v, o float32; products and softmax in fp32 */
@@ -83,10 +87,12 @@ typedef enum {
  *   causal  : 0 or 1.
  *   softmax_scale : finite and > 0; multiplies the fp32 scores (it is not
  *             folded into the stored Q).
- *   dtype   : FA_F32, FA_BF16 or FA_FP8_E4M3.  For FA_FP8_E4M3 the call
- *             allocates a stream-ordered workspace (hipMallocAsync /
- *             hipFreeAsync on `stream`) for the quantised Q, K and their
- *             scales, runs fa_quant_fp8_e4m3 on q and k, then the FP8 kernel.
+ *   dtype   : FA_F32, FA_BF16 or FA_FP8_E4M3.  For FA_BF16 and
+ *             FA_FP8_E4M3 the call allocates one stream-ordered workspace
+ *             (hipMallocAsync / hipFreeAsync on `stream`) for V transposed
+ *             (B*H*d*ceil(N/64)*64 bf16) and, for FA_FP8_E4M3, the quantised
+ *             Q, K and their scales (it runs fa_quant_fp8_e4m3 on q and k
+ *             before the FP8 kernel).  FA_F32 allocates nothing.
  * Returns FA_OK or the first error found.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -120,6 +126,29 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                      const void* v_bf16, void* o_bf16, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d,
                      int causal, float softmax_scale, void* stream);
+
+/*
+ * fa_bwd -- gradient of fa_fwd (FA_BF16 only).
+ *   q, k, v : the forward's bf16 inputs [B,H,N,d].
+ *   o       : the forward's bf16 output [B,H,N,d].
+ *   dout    : bf16 upstream gradient dL/dO [B,H,N,d].
+ *   lse     : float32 [B,H,N] as written by fa_fwd for the same inputs
+ *             (required, not NULL).
+ *   dq, dk, dv : bf16 outputs [B,H,N,d]; must not alias any input.
+ *   causal, softmax_scale : as given to fa_fwd.
+ *   dtype   : FA_BF16 (anything else returns FA_ERR_INVALID_DTYPE).
+ * With P = exp(softmax_scale * Q K^T [masked] - lse):
+ *   dV = P^T dO;  dP = dO V^T;  D_i = sum_k dO_ik O_ik;  dS = P * (dP - D);
+ *   dQ = softmax_scale * dS K;  dK = softmax_scale * dS^T Q.
+ * P and dS are rounded to bf16 for the matrix cores; accumulation is fp32.
+ * The call allocates one stream-ordered workspace (hipMallocAsync /
+ * hipFreeAsync on `stream`): Q, dO and K transposed (3*B*H*d*ceil(N/64)*64
+ * bf16) and two float32 [B,H,N] row statistics.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int64_t B, int64_t H, int64_t N, int64_t d,
+                 int causal, float softmax_scale, fa_dtype dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_string(fa_status s);

@@ -95,3 +95,32 @@ def test_python_wrapper_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(_binding, "_LIB_PATH", "/nonexistent/libfa.so")
     with pytest.raises(RuntimeError, match="not built"):
         _binding.load()
+
+
+def test_fa_bwd_rejects_bad_arguments(lib):
+    # q, k, v, o, dout, lse, dq, dk, dv at distinct fake addresses (never dereferenced:
+    # every case carries one invalid argument, so validation returns before any HIP call)
+    P = FAKE
+    ptrs = [P + 0x1000 * i for i in range(9)]
+
+    def call(i_over=None, val=None, B=1, H=1, N=64, d=64, causal=0, scale=0.125, dtype=1):
+        a = list(ptrs)
+        if i_over is not None:
+            a[i_over] = val
+        return lib.fa_bwd(*a, B, H, N, d, causal, scale, dtype, None)
+
+    for i in range(9):
+        assert call(i, 0) == 1, i                       # NULL pointer (lse included)
+    assert call(B=0) == 2
+    assert call(N=0) == 2
+    assert call(d=96) == 3
+    assert call(scale=0.0) == 4
+    assert call(scale=float("nan")) == 4
+    assert call(dtype=0) == 5                           # fp32 backward not provided
+    assert call(dtype=2) == 5
+    assert call(causal=2) == 7
+    assert call(6, ptrs[0]) == 7                        # dq aliases q
+    assert call(8, ptrs[4]) == 7                        # dv aliases dout
+    assert call(7, ptrs[6]) == 7                        # dk aliases dq
+    assert call(6, ptrs[6] + 8) == 6                    # misaligned dq
+    assert call(5, ptrs[5] + 2) == 6                    # misaligned lse

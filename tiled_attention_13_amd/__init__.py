@@ -1,8 +1,8 @@
-"""MI355X-native fused attention forward (FlashAttention forward pass on gfx950).
+"""MI355X-native fused attention (FlashAttention forward and backward on gfx950).
 
 The compute lives in ``libfa.so`` (hand-written HIP kernels behind the C ABI
 of ``include/fa.h``); this package only marshals torch tensors to it.
 """
-from ._binding import FAError, fwd, fwd_fp8, load, quant_fp8, status_string
+from ._binding import FAError, bwd, fwd, fwd_fp8, load, quant_fp8, status_string
 
-__all__ = ["FAError", "fwd", "fwd_fp8", "load", "quant_fp8", "status_string"]
+__all__ = ["FAError", "bwd", "fwd", "fwd_fp8", "load", "quant_fp8", "status_string"]

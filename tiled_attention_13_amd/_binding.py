@@ -1,8 +1,8 @@
 """ctypes binding of ``libfa.so`` (the C ABI in ``include/fa.h``).
 
 Argument marshalling only: tensors are passed as raw device pointers with
-the current torch stream; every step of the forward pass runs in the HIP
-kernels.  There is no fallback: if the library is missing or the call fails,
+the current torch stream; every step of the forward and backward passes
+runs in the HIP kernels.  There is no fallback: if the library is missing or the call fails,
 an exception is raised.
 """
 from __future__ import annotations
@@ -23,6 +23,7 @@ SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_quant_fp8_e4m3": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _P]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_abi_version": (_I, []),
 }
@@ -150,3 +151,30 @@ def fwd_fp8(q8, q_scale, k8, k_scale, v, causal: bool = False, softmax_scale: fl
                            B, H, N, d, int(bool(causal)), scale, _stream_ptr(stream))
     _check(st, "fa_fwd_fp8")
     return out, lse
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, softmax_scale: float | None = None,
+        dq=None, dk=None, dv=None, stream=None):
+    """Gradient of the attention forward through ``fa_bwd`` (bf16 only).
+
+    q, k, v, o, dout: contiguous bf16 device tensors ``[B, H, N, d]`` (o and
+    lse as returned by ``fwd`` for the same q, k, v, causal and scale).
+    Returns ``(dq, dk, dv)`` in bf16.
+    """
+    import torch
+    _check_qkv(q, k, v, torch.bfloat16)
+    for name, t in (("o", o), ("dout", dout)):
+        if not t.is_cuda or t.dtype != torch.bfloat16 or not t.is_contiguous() or t.shape != q.shape:
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor shaped like q")
+    B, H, N, d = q.shape
+    if lse is None or not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be the float32 [B, H, N] device tensor written by fwd")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                       B, H, N, d, int(bool(causal)), scale, FA_BF16, _stream_ptr(stream))
+    _check(st, "fa_bwd")
+    return dq, dk, dv

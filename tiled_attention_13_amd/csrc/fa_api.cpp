@@ -76,9 +76,9 @@ const char* fa_status_string(fa_status s) {
         case FA_ERR_INVALID_SHAPE: return "B, H, N must be >= 1 and B*H*N*d < 2^31";
         case FA_ERR_UNSUPPORTED_HEAD_DIM: return "head dim must be 32, 64 or 128";
         case FA_ERR_INVALID_SCALE: return "softmax_scale must be finite and > 0";
-        case FA_ERR_INVALID_DTYPE: return "unknown dtype";
+        case FA_ERR_INVALID_DTYPE: return "unknown or unsupported dtype";
         case FA_ERR_MISALIGNED: return "tensor pointers must be 16-byte aligned (lse/scales 4-byte)";
-        case FA_ERR_INVALID_ARGUMENT: return "invalid argument (causal must be 0 or 1; o must not alias inputs)";
+        case FA_ERR_INVALID_ARGUMENT: return "invalid argument (causal must be 0 or 1; outputs must not alias inputs)";
         case FA_ERR_UNSUPPORTED_ARCH: return "current device is not gfx950 (MI355X)";
         case FA_ERR_OUT_OF_MEMORY: return "device workspace allocation failed";
         case FA_ERR_LAUNCH: return "kernel launch failed";
@@ -189,6 +189,55 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                           softmax_scale};
             e = fa::launch_fwd(a, s);
         }
+    }
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return launch_status(e);
+    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                 int causal, float softmax_scale, fa_dtype dtype, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (dtype != FA_BF16) return FA_ERR_INVALID_DTYPE;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    const void* ins[] = {q, k, v, o, dout, lse};
+    const void* outs[] = {dq, dk, dv};
+    for (const void* x : outs) {
+        for (const void* y : ins)
+            if (x == y) return FA_ERR_INVALID_ARGUMENT;
+    }
+    if (dq == dk || dq == dv || dk == dv) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+        !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    const size_t tb = round_up(vt_bytes(BH, n, dd), 256);
+    const size_t vec = round_up(static_cast<size_t>(BH) * n * 4, 256);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, 3 * tb + 2 * vec, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return FA_ERR_OUT_OF_MEMORY;
+    }
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    void* qt = base;
+    void* dot = base + tb;
+    void* kt = base + 2 * tb;
+    float* lse2 = reinterpret_cast<float*>(base + 3 * tb);
+    float* dsum = reinterpret_cast<float*>(base + 3 * tb + vec);
+    hipError_t e = fa::launch_transpose_v(q, qt, BH, n, dd, s);
+    if (e == hipSuccess) e = fa::launch_transpose_v(dout, dot, BH, n, dd, s);
+    if (e == hipSuccess) e = fa::launch_transpose_v(k, kt, BH, n, dd, s);
+    if (e == hipSuccess) {
+        fa::BwdArgs a{q, k, v, o, dout, lse, qt, dot, kt, lse2, dsum, dq, dk, dv,
+                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+        e = fa::launch_bwd(a, s);
     }
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launch_status(e);

@@ -1,0 +1,560 @@
+// Attention backward for gfx950 (MI355X): dQ, dK, dV of
+// O = softmax(scale * Q K^T [causally masked]) V for an upstream gradient dO.
+//
+// The forward pass keeps no probabilities; the backward pass recomputes them
+// from Q, K and the per-row logsumexp the forward wrote (the Triton
+// walkthrough page, section 2.2: intermediate results are recomputed in the
+// backward pass instead of stored).  With P = exp(scale * S - lse):
+//
+//   dV = P^T dO,   dP = dO V^T,   D_i = sum_k dO_ik O_ik,
+//   dS = P * (dP - D),   dQ = scale * dS K,   dK = scale * dS^T Q.
+//
+// Work is split so that no two workgroups write the same output row (the tag
+// page, excerpt on V2: the work of the backward pass is reassigned to cut
+// synchronisation between thread blocks):
+//
+//  * bwd_prep_kernel: D_i and lse_i * log2(e) per query row.
+//  * bwd_dq_kernel: query-stationary, the forward's layout.  A workgroup
+//    holds 256 queries (32 per wave, Q and dO in registers as MFMA B
+//    operands) and streams 64-key tiles of K, V and K^T through LDS;
+//    S^T = K Q^T and dP^T = V dO^T give every lane the scores of one query,
+//    so lse and D are one value per lane, and dS^T lands in the B-operand
+//    layout of dQ^T += K^T dS^T.
+//  * bwd_dkdv_kernel: key-stationary.  A workgroup holds 128 keys (32 per
+//    wave, K and V in registers) and streams 64-query tiles of Q, dO, Q^T,
+//    dO^T, lse and D through LDS; S = Q K^T and dP = dO V^T give every lane
+//    the scores of one key, and P and dS land in the B-operand layout of
+//    dV^T += dO^T P and dK^T += Q^T dS.
+//
+// The transposed operands (K^T, Q^T, dO^T) come from the same pre-pass the
+// forward uses for V^T, with rows permuted within each 16-group so that a
+// 16-byte LDS read feeds one MFMA A operand.  P and dS are rounded to bf16
+// for the MFMAs; everything else accumulates in fp32.  Causal: tiles that
+// lie entirely above the diagonal are skipped, and only tiles that cross it
+// (or the sequence end) compare indices.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+struct BParams {
+    const uint8_t* q;
+    const uint8_t* k;
+    const uint8_t* v;
+    const uint8_t* dout;
+    const uint8_t* qt;       // Q^T  [BH, D, np], rows permuted within each 16-group
+    const uint8_t* dot;      // dO^T [BH, D, np]
+    const uint8_t* kt;       // K^T  [BH, D, np]
+    const float* lse2;       // lse * log2(e)   [BH, N]
+    const float* dsum;       // D = rowsum(dO * O) [BH, N]
+    uint8_t* dq;
+    uint8_t* dk;
+    uint8_t* dv;
+    int BH;
+    int N;
+    int np;
+    int n_tiles;             // workgroups per (b, h)
+    float c_log2;            // softmax_scale * log2(e)
+    float scale;
+};
+
+// ===========================================================================
+// Pre-pass: D_i = sum_k dO_ik O_ik and lse_i * log2(e), one row per group of
+// D/8 lanes (16 bytes of O and dO per lane).
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ o, const uint8_t* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ lse2,
+                                                       float* __restrict__ dsum, long long rows) {
+    constexpr int LPR = D / 8;                           // lanes per row
+    const long long row = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    float acc = 0.0f;
+    if (row < rows) {
+        const size_t off = (static_cast<size_t>(row) * D + 8 * part) * 2;
+        const u32x4 a = ld16(o + off), b = ld16(dout + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc = fmaf(__uint_as_float(a[e] << 16), __uint_as_float(b[e] << 16), acc);
+            acc = fmaf(__uint_as_float(a[e] & 0xFFFF0000u), __uint_as_float(b[e] & 0xFFFF0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, LPR);
+    if (row < rows && part == 0) {
+        dsum[row] = acc;
+        lse2[row] = lse[row] * kLog2e;
+    }
+}
+
+// ===========================================================================
+// dQ: 8 waves x 32 queries, 64-key tiles of K, V and K^T in a 2-stage LDS ring.
+// ===========================================================================
+template <int D>
+struct DqCfg {
+    static constexpr int NW = 8;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BM = 32 * NW;
+    static constexpr int BN = kKeyTile;
+    static constexpr int KROW = 2 * D + 16;              // bytes per K / V row in LDS (padded)
+    static constexpr int TROW = 2 * BN + 16;             // bytes per K^T row in LDS (padded)
+    static constexpr int KBYTES = BN * KROW;
+    static constexpr int TBYTES = D * TROW;
+    static constexpr int STAGE = 2 * KBYTES + TBYTES;
+    static constexpr int R_CPR = D / 8;                  // 16-byte chunks per K / V row
+    static constexpr int R_CHUNKS = BN * R_CPR;
+    static constexpr int T_CPR = 2 * BN / 16;            // 16-byte chunks per K^T row
+    static constexpr int T_CHUNKS = D * T_CPR;
+    static constexpr int R_PER_T = (R_CHUNKS + NT - 1) / NT;
+    static constexpr int T_PER_T = (T_CHUNKS + NT - 1) / NT;
+    static constexpr int QREGS = D / 16;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
+    using C = DqCfg<D>;
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    int qt = blockIdx.x / p.BH;
+    const int bh = blockIdx.x - qt * p.BH;
+    if (CAUSAL) qt = p.n_tiles - 1 - qt;                 // heaviest query tiles first
+    const int q0 = qt * BM, qw0 = q0 + 32 * w, my_q = qw0 + l32;
+
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* kg = p.k + slice * 2;
+    const uint8_t* vg = p.v + slice * 2;
+    const uint8_t* ktg = p.kt + static_cast<size_t>(bh) * D * p.np * 2;
+
+    // Q and dO rows of this lane's query: B operands (k-slots = d)
+    u32x4 qf[C::QREGS], gf[C::QREGS];
+    float lse2_q = 0.0f, d_q = 0.0f;
+    {
+        const bool ok = my_q < N;
+        const size_t off = (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i) {
+            qf[i] = ok ? ld16(p.q + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+            gf[i] = ok ? ld16(p.dout + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+        }
+        if (ok) {
+            lse2_q = p.lse2[static_cast<size_t>(bh) * N + my_q];
+            d_q = p.dsum[static_cast<size_t>(bh) * N + my_q];
+        }
+    }
+
+    const int n_all = (N + BN - 1) / BN;
+    const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
+    const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
+
+    u32x4 kst[C::R_PER_T], vst[C::R_PER_T], tst[C::T_PER_T];
+    auto load_tile = [&](int t) {
+        const int n0 = t * BN;
+#pragma unroll
+        for (int i = 0; i < C::R_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::R_CHUNKS) {
+                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+                const bool ok = n0 + row < N;
+                const size_t off = (static_cast<size_t>(n0 + row) * D + 8 * col) * 2;
+                kst[i] = ok ? ld16(kg + off) : u32x4{0, 0, 0, 0};
+                vst[i] = ok ? ld16(vg + off) : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::T_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::T_CHUNKS) {
+                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+                tst[i] = ld16(ktg + (static_cast<size_t>(d) * p.np + n0) * 2 + 16 * col);
+            }
+        }
+    };
+    auto store_tile = [&](int t) {
+        uint8_t* ks = smem + (t & 1) * C::STAGE;
+        uint8_t* vs = ks + C::KBYTES;
+        uint8_t* ts = vs + C::KBYTES;
+#pragma unroll
+        for (int i = 0; i < C::R_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::R_CHUNKS) {
+                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+                *reinterpret_cast<u32x4*>(ks + row * C::KROW + 16 * col) = kst[i];
+                *reinterpret_cast<u32x4*>(vs + row * C::KROW + 16 * col) = vst[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::T_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::T_CHUNKS) {
+                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+                *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
+            }
+        }
+    };
+
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+    auto compute = [&](int j, bool masked) {
+        const uint8_t* ks = smem + (j & 1) * C::STAGE;
+        const uint8_t* vs = ks + C::KBYTES;
+        const uint8_t* ts = vs + C::KBYTES;
+        const int n0 = j * BN;
+        float ds[BN / 2];
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            f32x16 s = {}, dp = {};
+            const uint8_t* kr = ks + (32 * kb + l32) * C::KROW + 16 * h;
+            const uint8_t* vr = vs + (32 * kb + l32) * C::KROW + 16 * h;
+#pragma unroll
+            for (int i = 0; i < C::QREGS; ++i) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(kr + 32 * i)),
+                                                           __builtin_bit_cast(bf16x8, qf[i]), s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(vr + 32 * i)),
+                                                            __builtin_bit_cast(bf16x8, gf[i]), dp, 0, 0, 0);
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float pr = fast_exp2(fmaf(s[v], p.c_log2, -lse2_q));
+                if (masked) {
+                    const int key = n0 + 32 * kb + acc_row(v, h);
+                    if (key >= N || (CAUSAL && key > my_q)) pr = 0.0f;
+                }
+                ds[16 * kb + v] = pr * (dp[v] - d_q);
+            }
+        }
+        bf16x8 dsf[BN / 16];
+#pragma unroll
+        for (int cc = 0; cc < BN / 16; ++cc)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dsf[cc][t] = static_cast<__bf16>(ds[8 * cc + t]);
+        const uint8_t* tr = ts + l32 * C::TROW + 16 * h;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * cc)), dsf[cc], dq[db], 0, 0, 0);
+    };
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int j = 0; j < n_kt; ++j) {
+        if (j + 1 < n_kt) load_tile(j + 1);
+        if (j < j_last) {
+            compute(j, false);
+        } else if (j == j_last) {
+            const int n0 = j * BN;
+            compute(j, (CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N);
+        }
+        if (j + 1 < n_kt) store_tile(j + 1);
+        __syncthreads();
+    }
+
+    if (my_q < N) {
+        uint8_t* orow = p.dq + (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(dq[db][4 * g + e] * p.scale);
+                *reinterpret_cast<bf16x4*>(orow + 2 * (32 * db + 8 * g + 4 * h)) = out;
+            }
+    }
+}
+
+// ===========================================================================
+// dK, dV: 4 waves x 32 keys, 64-query tiles of Q, dO, Q^T, dO^T, lse and D
+// in a 2-stage LDS ring.  One wave per SIMD (the accumulators of dK and dV
+// and the K and V operands take most of the register file).
+// ===========================================================================
+template <int D>
+struct DkvCfg {
+    static constexpr int NW = 4;
+    static constexpr int NT = 64 * NW;
+    static constexpr int BK = 32 * NW;                   // keys per workgroup
+    static constexpr int BQ = 64;                        // queries per tile
+    static constexpr int RROW = 2 * D + 16;              // bytes per Q / dO row in LDS (padded)
+    static constexpr int TROW = 2 * BQ + 16;             // bytes per Q^T / dO^T row in LDS (padded)
+    static constexpr int RBYTES = BQ * RROW;
+    static constexpr int TBYTES = D * TROW;
+    static constexpr int VEC = BQ * 4;                   // lse2 or D of one tile, bytes
+    static constexpr int STAGE = 2 * RBYTES + 2 * TBYTES + 2 * VEC;
+    static constexpr int R_CPR = D / 8;
+    static constexpr int R_CHUNKS = BQ * R_CPR;
+    static constexpr int T_CPR = 2 * BQ / 16;
+    static constexpr int T_CHUNKS = D * T_CPR;
+    static constexpr int V_CHUNKS = 2 * VEC / 16;        // lse2 then D
+    static constexpr int R_PER_T = (R_CHUNKS + NT - 1) / NT;
+    static constexpr int T_PER_T = (T_CHUNKS + NT - 1) / NT;
+    static constexpr int QREGS = D / 16;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
+    using C = DkvCfg<D>;
+    constexpr int BK = C::BK, BQ = C::BQ, NT = C::NT;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    const int kt = blockIdx.x / p.BH;                    // causal: low key tiles see the most queries
+    const int bh = blockIdx.x - kt * p.BH;
+    const int k0 = kt * BK, kw0 = k0 + 32 * w, my_k = kw0 + l32;
+
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* qg = p.q + slice * 2;
+    const uint8_t* gg = p.dout + slice * 2;
+    const uint8_t* qtg = p.qt + static_cast<size_t>(bh) * D * p.np * 2;
+    const uint8_t* gtg = p.dot + static_cast<size_t>(bh) * D * p.np * 2;
+    const float* l2g = p.lse2 + static_cast<size_t>(bh) * N;
+    const float* dsg = p.dsum + static_cast<size_t>(bh) * N;
+
+    // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
+    u32x4 kf[C::QREGS], vf[C::QREGS];
+    {
+        const bool ok = my_k < N;
+        const size_t off = (slice + static_cast<size_t>(my_k) * D) * 2;
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i) {
+            kf[i] = ok ? ld16(p.k + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+            vf[i] = ok ? ld16(p.v + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+        }
+    }
+
+    const int n_qt = (N + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? min(k0 / BQ, n_qt) : 0;
+    // first tile holding a query at or after this wave's first key
+    const int t_first = CAUSAL ? max(t0, kw0 / BQ) : 0;
+
+    u32x4 qst[C::R_PER_T], gst[C::R_PER_T], qtst[C::T_PER_T], gtst[C::T_PER_T], vecst;
+    auto load_tile = [&](int t) {
+        const int m0 = t * BQ;
+#pragma unroll
+        for (int i = 0; i < C::R_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::R_CHUNKS) {
+                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+                const bool ok = m0 + row < N;
+                const size_t off = (static_cast<size_t>(m0 + row) * D + 8 * col) * 2;
+                qst[i] = ok ? ld16(qg + off) : u32x4{0, 0, 0, 0};
+                gst[i] = ok ? ld16(gg + off) : u32x4{0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::T_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::T_CHUNKS) {
+                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+                const size_t off = (static_cast<size_t>(d) * p.np + m0) * 2 + 16 * col;
+                qtst[i] = ld16(qtg + off);
+                gtst[i] = ld16(gtg + off);
+            }
+        }
+        if (tid < C::V_CHUNKS) {
+            // 4 rows per chunk; rows past the end get lse2 = +inf (P = 0) and D = 0
+            const int which = tid / (C::VEC / 16), r0 = m0 + 4 * (tid - which * (C::VEC / 16));
+            const float* src = which == 0 ? l2g : dsg;
+            const float fill = which == 0 ? __builtin_inff() : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vecst[e] = __float_as_uint(r0 + e < N ? src[r0 + e] : fill);
+        }
+    };
+    auto store_tile = [&](int t) {
+        uint8_t* qs = smem + (t & 1) * C::STAGE;
+        uint8_t* gs = qs + C::RBYTES;
+        uint8_t* qts = gs + C::RBYTES;
+        uint8_t* gts = qts + C::TBYTES;
+        uint8_t* vs = gts + C::TBYTES;
+#pragma unroll
+        for (int i = 0; i < C::R_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::R_CHUNKS) {
+                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+                *reinterpret_cast<u32x4*>(qs + row * C::RROW + 16 * col) = qst[i];
+                *reinterpret_cast<u32x4*>(gs + row * C::RROW + 16 * col) = gst[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C::T_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::T_CHUNKS) {
+                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+                *reinterpret_cast<u32x4*>(qts + d * C::TROW + 16 * col) = qtst[i];
+                *reinterpret_cast<u32x4*>(gts + d * C::TROW + 16 * col) = gtst[i];
+            }
+        }
+        if (tid < C::V_CHUNKS) *reinterpret_cast<u32x4*>(vs + 16 * tid) = vecst;
+    };
+
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    auto compute = [&](int t, bool masked) {
+        const uint8_t* qs = smem + (t & 1) * C::STAGE;
+        const uint8_t* gs = qs + C::RBYTES;
+        const uint8_t* qts = gs + C::RBYTES;
+        const uint8_t* gts = qts + C::TBYTES;
+        const float* l2s = reinterpret_cast<const float*>(gts + C::TBYTES);
+        const float* dss = l2s + BQ;
+        const int m0 = t * BQ;
+        float pv[BQ / 2], dsv[BQ / 2];
+#pragma unroll
+        for (int qb = 0; qb < BQ / 32; ++qb) {
+            f32x16 s = {}, dp = {};
+            const uint8_t* qr = qs + (32 * qb + l32) * C::RROW + 16 * h;
+            const uint8_t* gr = gs + (32 * qb + l32) * C::RROW + 16 * h;
+#pragma unroll
+            for (int i = 0; i < C::QREGS; ++i) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(qr + 32 * i)),
+                                                           __builtin_bit_cast(bf16x8, kf[i]), s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(gr + 32 * i)),
+                                                            __builtin_bit_cast(bf16x8, vf[i]), dp, 0, 0, 0);
+            }
+            // rows of register v: query 32*qb + 8*(v/4) + 4*h + v%4, four at a time
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * qb + 8 * g + 4 * h);
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g + e;
+                    float pr = fast_exp2(fmaf(s[v], p.c_log2, -l4[e]));
+                    if (masked && CAUSAL && my_k > m0 + 32 * qb + acc_row(v, h)) pr = 0.0f;
+                    pv[16 * qb + v] = pr;
+                    dsv[16 * qb + v] = pr * (dp[v] - d4[e]);
+                }
+            }
+        }
+        bf16x8 pf[BQ / 16], dsf[BQ / 16];
+#pragma unroll
+        for (int cc = 0; cc < BQ / 16; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pf[cc][e] = static_cast<__bf16>(pv[8 * cc + e]);
+                dsf[cc][e] = static_cast<__bf16>(dsv[8 * cc + e]);
+            }
+        const uint8_t* gtr = gts + l32 * C::TROW + 16 * h;
+        const uint8_t* qtr = qts + l32 * C::TROW + 16 * h;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < BQ / 16; ++cc) {
+                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, ld16(gtr + 32 * db * C::TROW + 32 * cc)), pf[cc], dv[db], 0, 0, 0);
+                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, ld16(qtr + 32 * db * C::TROW + 32 * cc)), dsf[cc], dk[db], 0, 0, 0);
+            }
+    };
+
+    if (t0 < n_qt) {
+        load_tile(t0);
+        store_tile(t0);
+    }
+    __syncthreads();
+    for (int t = t0; t < n_qt; ++t) {
+        if (t + 1 < n_qt) load_tile(t + 1);
+        if (t >= t_first) {
+            // a causal mask is needed while the tile starts before this wave's last key
+            const int m0 = t * BQ;
+            if (CAUSAL && m0 < kw0 + 31) compute(t, true);
+            else compute(t, false);
+        }
+        if (t + 1 < n_qt) store_tile(t + 1);
+        __syncthreads();
+    }
+
+    if (my_k < N) {
+        const size_t off = (slice + static_cast<size_t>(my_k) * D) * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 ok_, ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ok_[e] = static_cast<__bf16>(dk[db][4 * g + e] * p.scale);
+                    ov[e] = static_cast<__bf16>(dv[db][4 * g + e]);
+                }
+                *reinterpret_cast<bf16x4*>(p.dk + off + 2 * (32 * db + 8 * g + 4 * h)) = ok_;
+                *reinterpret_cast<bf16x4*>(p.dv + off + 2 * (32 * db + 8 * g + 4 * h)) = ov;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_d(BParams bp, const void* o, const float* lse, float* lse2, float* dsum, hipStream_t st) {
+    const long long rows = static_cast<long long>(bp.BH) * bp.N;
+    const long long pgrid = (rows * (D / 8) + 255) / 256;
+    if (pgrid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_prep_kernel<D>, dim3(static_cast<int>(pgrid)), dim3(256), 0, st,
+                       static_cast<const uint8_t*>(o), bp.dout, lse, lse2, dsum, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    BParams a = bp;
+    a.n_tiles = (bp.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
+    const long long g1 = static_cast<long long>(a.n_tiles) * bp.BH;
+    BParams b = bp;
+    b.n_tiles = (bp.N + DkvCfg<D>::BK - 1) / DkvCfg<D>::BK;
+    const long long g2 = static_cast<long long>(b.n_tiles) * bp.BH;
+    if (g1 > 0x7FFFFFFFLL || g2 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(static_cast<int>(g2)), dim3(DkvCfg<D>::NT), 0, st, b);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<int>(g1)), dim3(DqCfg<D>::NT), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+    BParams bp;
+    bp.q = static_cast<const uint8_t*>(a.q);
+    bp.k = static_cast<const uint8_t*>(a.k);
+    bp.v = static_cast<const uint8_t*>(a.v);
+    bp.dout = static_cast<const uint8_t*>(a.dout);
+    bp.qt = static_cast<const uint8_t*>(a.qt);
+    bp.dot = static_cast<const uint8_t*>(a.dot);
+    bp.kt = static_cast<const uint8_t*>(a.kt);
+    bp.lse2 = a.lse2;
+    bp.dsum = a.dsum;
+    bp.dq = static_cast<uint8_t*>(a.dq);
+    bp.dk = static_cast<uint8_t*>(a.dk);
+    bp.dv = static_cast<uint8_t*>(a.dv);
+    bp.BH = a.BH;
+    bp.N = a.N;
+    bp.np = a.np;
+    bp.n_tiles = 0;
+    bp.c_log2 = a.softmax_scale * kLog2e;
+    bp.scale = a.softmax_scale;
+    switch (a.d) {
+        case 32: return a.causal ? launch_bwd_d<32, true>(bp, a.o, a.lse, a.lse2, a.dsum, stream)
+                                 : launch_bwd_d<32, false>(bp, a.o, a.lse, a.lse2, a.dsum, stream);
+        case 64: return a.causal ? launch_bwd_d<64, true>(bp, a.o, a.lse, a.lse2, a.dsum, stream)
+                                 : launch_bwd_d<64, false>(bp, a.o, a.lse, a.lse2, a.dsum, stream);
+        case 128: return a.causal ? launch_bwd_d<128, true>(bp, a.o, a.lse, a.lse2, a.dsum, stream)
+                                  : launch_bwd_d<128, false>(bp, a.o, a.lse, a.lse2, a.dsum, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fa

@@ -1,0 +1,75 @@
+// Device helpers shared by the forward and backward attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Max / sum with the lane 32 apart (v_permlane32_swap: both halves see both values).
+__device__ __forceinline__ float max_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    uint32_t u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row of the 32x32 MFMA accumulator held in register v of a lane in half h.
+__device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+// LDS column of key `kk` (0..63) inside a V^T row.  Keys are permuted within
+// each group of 16 so that the eight keys one lane contracts over in a P*V
+// MFMA are adjacent (one 16-byte read); see the P fragment layout below.
+__device__ __forceinline__ int vt_slot(int kk) {
+    const int c = kk >> 4, a = (kk >> 3) & 1, hh = (kk >> 2) & 1, b = kk & 3;
+    return 16 * c + 8 * hh + 4 * a + b;
+}
+
+// Scheduling pattern for a block of N (16-byte LDS read -> MFMA) pairs: issue
+// AHEAD reads first, then alternate one MFMA with one further read, so each
+// MFMA's operand was requested about AHEAD MFMAs (~32 cycles each) earlier.
+constexpr int kLdsAhead = 6;
+template <int N, int AHEAD>
+__device__ __forceinline__ void pipeline_lds_mfma() {
+    constexpr int A = AHEAD < N ? AHEAD : N;
+    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
+// Barrier that orders LDS traffic only: outstanding global loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace
+}  // namespace fa

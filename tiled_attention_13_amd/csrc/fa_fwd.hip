@@ -13,8 +13,8 @@
 // scores of ONE query (the other 16 of each 32-key block sit in lane l ^ 32).
 // Row reductions are in-lane plus one v_permlane32_swap, and the
 // probabilities already sit where the B operand of O^T += V^T P^T wants
-// them: P never goes through LDS.  V^T is produced while tiles are copied
-// into LDS.
+// them: P never goes through LDS.  V^T comes from a pre-pass that
+// transposes V once per call (keys permuted within each tile to match).
 //
 // Online softmax (Triton walkthrough page, section 2.1): running max m and
 // running sum l per query, kept in base-2 units with softmax_scale*log2(e)
@@ -36,22 +36,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kNegInf = -__builtin_inff();
 
 struct KParams {
     const uint8_t* q;
@@ -68,27 +57,6 @@ struct KParams {
     int n_qtiles;
     float c_log2;       // softmax_scale * log2(e)
 };
-
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
-    return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Max / sum with the lane 32 apart (v_permlane32_swap: both halves see both values).
-__device__ __forceinline__ float max_halves(float x) {
-    uint32_t u = __float_as_uint(x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-    uint32_t u = __float_as_uint(x);
-    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Row of the 32x32 MFMA accumulator held in register v of a lane in half h.
-__device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
 // ---------------------------------------------------------------------------
 // Online-softmax step on the scores one lane holds for its query.
@@ -125,14 +93,6 @@ __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m,
     }
     l = fmaf(l, alpha, rs);
     return alpha;
-}
-
-// LDS column of key `kk` (0..63) inside a V^T row.  Keys are permuted within
-// each group of 16 so that the eight keys one lane contracts over in a P*V
-// MFMA are adjacent (one 16-byte read); see the P fragment layout below.
-__device__ __forceinline__ int vt_slot(int kk) {
-    const int c = kk >> 4, a = (kk >> 3) & 1, hh = (kk >> 2) & 1, b = kk & 3;
-    return 16 * c + 8 * hh + 4 * a + b;
 }
 
 // ===========================================================================
@@ -177,29 +137,6 @@ struct PPCfg {
     static constexpr bool F8N = FP8 && !F8W;
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
-
-// Scheduling pattern for a block of N (16-byte LDS read -> MFMA) pairs: issue
-// AHEAD reads first, then alternate one MFMA with one further read, so each
-// MFMA's operand was requested about AHEAD MFMAs (~32 cycles each) earlier.
-constexpr int kLdsAhead = 6;
-template <int N, int AHEAD>
-__device__ __forceinline__ void pipeline_lds_mfma() {
-    constexpr int A = AHEAD < N ? AHEAD : N;
-    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
-#pragma unroll
-    for (int i = 0; i < N - A; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
-}
-
-// Barrier that orders LDS traffic only: outstanding global loads stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 template <int D, bool CAUSAL, bool FP8>
 __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {

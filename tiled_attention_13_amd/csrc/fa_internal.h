@@ -37,6 +37,32 @@ constexpr int kKeyTile = 64;
 // attention kernel's LDS layout uses.  vt must hold BH * d * np bf16 values.
 hipError_t launch_transpose_v(const void* v, void* vt, int BH, int N, int d, hipStream_t stream);
 
+struct BwdArgs {
+    const void* q;          // bf16 [BH, N, d]
+    const void* k;
+    const void* v;
+    const void* o;          // forward output
+    const void* dout;       // upstream gradient
+    const float* lse;       // forward logsumexp [BH, N]
+    const void* qt;         // Q^T, dO^T, K^T from launch_transpose_v, [BH, d, np] each
+    const void* dot;
+    const void* kt;
+    float* lse2;            // workspace [BH, N]: lse * log2(e)
+    float* dsum;            // workspace [BH, N]: rowsum(dO * O)
+    void* dq;               // bf16 [BH, N, d]
+    void* dk;
+    void* dv;
+    int BH;
+    int N;
+    int np;
+    int d;
+    bool causal;
+    float softmax_scale;
+};
+
+// Enqueue the backward kernels (row statistics, dK/dV, dQ) on `stream`.
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
 // Enqueue the per-64-row-tile e4m3fn quantisation of a bf16 [BH, N, d] tensor.
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale,
                             int BH, int N, int d, hipStream_t stream);

@@ -141,3 +141,12 @@ def digest(*arrays: np.ndarray) -> str:
     for a in arrays:
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
+
+
+def make_grad(w: Workload, seed: int | None = None, shape: tuple | None = None):
+    """Upstream gradient dO for the backward pass: standard normal, rounded to
+    bf16, from its own stream (PCG64 seeded with ``seed`` or ``w.seed``
+    + 1_000_003), so the forward inputs of a workload stay unchanged."""
+    shp = tuple(shape) if shape is not None else w.shape
+    rng = np.random.Generator(np.random.PCG64((w.seed if seed is None else seed) + 1_000_003))
+    return round_to_bf16(rng.standard_normal(shp, dtype=np.float32))
