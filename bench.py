@@ -7,7 +7,13 @@ halved for causal), ms per call, the roofline entry of the attention kernel
 and the float64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4_bf16]
-                    [--no-cpu-baseline] [--calib-copy-mib M]
+                    [--no-cpu-baseline] [--no-bwd] [--calib-copy-mib M]
+
+The line also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
+seeded upstream gradient) timed the same way on the same bf16 workload,
+with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
+matrix-core FLOPs the kernels actually execute (3.5 x: the dQ kernel
+recomputes S and dP).
 
 ``--calib-copy-mib`` runs, after the timed loop, a plain device copy of M MiB
 so that a counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) sees a kernel
@@ -88,6 +94,36 @@ def cpu_baseline(w, q, k, v, budget_s: float):
             "seconds": round(dt, 2), "cpu_model": _cpu_model()}
 
 
+def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
+    """Time fa_bwd on the resident forward inputs, output and lse (one call = one step)."""
+    import torch
+    from tiled_attention_13_amd import bwd
+    from tiled_attention_13_amd.inputs import make_grad
+    g = torch.from_numpy(make_grad(w)).to("cuda").to(torch.bfloat16)
+    gq, gk, gv = (torch.empty_like(tq) for _ in range(3))
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        bwd(tq, tk, tv, o, g, lse, causal=w.causal, dq=gq, dk=gk, dv=gv)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        bwd(tq, tk, tv, o, g, lse, causal=w.causal, dq=gq, dk=gk, dv=gv)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_call = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms = float(per_call.mean())
+    conv = 2.5 * w.flops()
+    executed = 3.5 * w.flops()
+    return {"ms_per_call": round(ms, 4), "median_ms": round(float(np.median(per_call)), 4),
+            "tflops": round(conv / (ms * 1e-3) / 1e12, 2),
+            "flop_convention": "2.5 x forward FLOPs (dV, dP, dQ, dK plus the recomputed S)",
+            "mfma_tflops_executed": round(executed / (ms * 1e-3) / 1e12, 2),
+            "pct_mfma_peak": round(100.0 * executed / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2),
+            "kernels": "bwd_prep_kernel, 3 x transpose_v_kernel, bwd_dkdv_kernel, bwd_dq_kernel"}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -108,6 +144,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0)
+    ap.add_argument("--no-bwd", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -194,6 +231,8 @@ def main():
         "input_sha256": digest(q, k, v)[:16],
         "input_gen_s": round(gen_s, 2),
     }
+    if not args.no_bwd and w.dtype == "bf16":
+        result["backward"] = bench_backward(w, dq, dk, dv, out, lse, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -252,11 +252,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
     __syncthreads();
     for (int j = 0; j < n_kt; ++j) {
         if (j + 1 < n_kt) load_tile(j + 1);
-        if (j < j_last) {
-            compute(j, false);
-        } else if (j == j_last) {
+        if (j <= j_last) {
+            // only the last tile of this wave can cross the diagonal or the sequence end
             const int n0 = j * BN;
-            compute(j, (CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N);
+            compute(j, j == j_last && ((CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N));
         }
         if (j + 1 < n_kt) store_tile(j + 1);
         __syncthreads();
@@ -342,18 +341,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
     // first tile holding a query at or after this wave's first key
     const int t_first = CAUSAL ? max(t0, kw0 / BQ) : 0;
 
-    u32x4 qst[C::R_PER_T], gst[C::R_PER_T], qtst[C::T_PER_T], gtst[C::T_PER_T], vecst;
-    auto load_tile = [&](int t) {
+    // A tile is copied in two parts (part 0: Q rows, Q^T, lse2 and D; part 1:
+    // dO rows, dO^T), each loaded from global memory just before one 32-query
+    // block of the current tile is computed and written to LDS right after it,
+    // so only half a tile is ever staged in registers.
+    u32x4 rst[C::R_PER_T], tst[C::T_PER_T], vecst;
+    auto load_part = [&](int t, int part) {
         const int m0 = t * BQ;
+        const uint8_t* rg = part == 0 ? qg : gg;
+        const uint8_t* tg = part == 0 ? qtg : gtg;
 #pragma unroll
         for (int i = 0; i < C::R_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::R_CHUNKS) {
                 const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                const bool ok = m0 + row < N;
                 const size_t off = (static_cast<size_t>(m0 + row) * D + 8 * col) * 2;
-                qst[i] = ok ? ld16(qg + off) : u32x4{0, 0, 0, 0};
-                gst[i] = ok ? ld16(gg + off) : u32x4{0, 0, 0, 0};
+                rst[i] = m0 + row < N ? ld16(rg + off) : u32x4{0, 0, 0, 0};
             }
         }
 #pragma unroll
@@ -361,12 +364,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
             const int c = i * NT + tid;
             if (c < C::T_CHUNKS) {
                 const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                const size_t off = (static_cast<size_t>(d) * p.np + m0) * 2 + 16 * col;
-                qtst[i] = ld16(qtg + off);
-                gtst[i] = ld16(gtg + off);
+                tst[i] = ld16(tg + (static_cast<size_t>(d) * p.np + m0) * 2 + 16 * col);
             }
         }
-        if (tid < C::V_CHUNKS) {
+        if (part == 0 && tid < C::V_CHUNKS) {
             // 4 rows per chunk; rows past the end get lse2 = +inf (P = 0) and D = 0
             const int which = tid / (C::VEC / 16), r0 = m0 + 4 * (tid - which * (C::VEC / 16));
             const float* src = which == 0 ? l2g : dsg;
@@ -375,19 +376,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
             for (int e = 0; e < 4; ++e) vecst[e] = __float_as_uint(r0 + e < N ? src[r0 + e] : fill);
         }
     };
-    auto store_tile = [&](int t) {
-        uint8_t* qs = smem + (t & 1) * C::STAGE;
-        uint8_t* gs = qs + C::RBYTES;
-        uint8_t* qts = gs + C::RBYTES;
-        uint8_t* gts = qts + C::TBYTES;
-        uint8_t* vs = gts + C::TBYTES;
+    auto store_part = [&](int t, int part) {
+        uint8_t* stage = smem + (t & 1) * C::STAGE;
+        uint8_t* rs = stage + part * C::RBYTES;
+        uint8_t* ts = stage + 2 * C::RBYTES + part * C::TBYTES;
 #pragma unroll
         for (int i = 0; i < C::R_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::R_CHUNKS) {
                 const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                *reinterpret_cast<u32x4*>(qs + row * C::RROW + 16 * col) = qst[i];
-                *reinterpret_cast<u32x4*>(gs + row * C::RROW + 16 * col) = gst[i];
+                *reinterpret_cast<u32x4*>(rs + row * C::RROW + 16 * col) = rst[i];
             }
         }
 #pragma unroll
@@ -395,11 +393,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
             const int c = i * NT + tid;
             if (c < C::T_CHUNKS) {
                 const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                *reinterpret_cast<u32x4*>(qts + d * C::TROW + 16 * col) = qtst[i];
-                *reinterpret_cast<u32x4*>(gts + d * C::TROW + 16 * col) = gtst[i];
+                *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
             }
         }
-        if (tid < C::V_CHUNKS) *reinterpret_cast<u32x4*>(vs + 16 * tid) = vecst;
+        if (part == 0 && tid < C::V_CHUNKS)
+            *reinterpret_cast<u32x4*>(stage + 2 * C::RBYTES + 2 * C::TBYTES + 16 * tid) = vecst;
     };
 
     f32x16 dk[D / 32], dv[D / 32];
@@ -409,45 +407,44 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
         dv[db] = f32x16{};
     }
 
-    auto compute = [&](int t, bool masked) {
+    // one 32-query block qb of tile t: S and dP, then its share of dV and dK
+    auto compute = [&](int t, int qb, bool masked) {
         const uint8_t* qs = smem + (t & 1) * C::STAGE;
         const uint8_t* gs = qs + C::RBYTES;
         const uint8_t* qts = gs + C::RBYTES;
         const uint8_t* gts = qts + C::TBYTES;
         const float* l2s = reinterpret_cast<const float*>(gts + C::TBYTES);
         const float* dss = l2s + BQ;
-        const int m0 = t * BQ;
-        float pv[BQ / 2], dsv[BQ / 2];
+        // causal: key my_k is masked for query row 32*qb + 8*(v/4) + 4*h + v%4 of the tile when
+        // rel > 8*(v/4) + v%4
+        const int rel = my_k - t * BQ - 32 * qb - 4 * h;
+        f32x16 s = {}, dp = {};
+        const uint8_t* qr = qs + (32 * qb + l32) * C::RROW + 16 * h;
+        const uint8_t* gr = gs + (32 * qb + l32) * C::RROW + 16 * h;
 #pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb) {
-            f32x16 s = {}, dp = {};
-            const uint8_t* qr = qs + (32 * qb + l32) * C::RROW + 16 * h;
-            const uint8_t* gr = gs + (32 * qb + l32) * C::RROW + 16 * h;
+        for (int i = 0; i < C::QREGS; ++i) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(qr + 32 * i)),
+                                                       __builtin_bit_cast(bf16x8, kf[i]), s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(gr + 32 * i)),
+                                                        __builtin_bit_cast(bf16x8, vf[i]), dp, 0, 0, 0);
+        }
+        float pv[16], dsv[16];
 #pragma unroll
-            for (int i = 0; i < C::QREGS; ++i) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(qr + 32 * i)),
-                                                           __builtin_bit_cast(bf16x8, kf[i]), s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(gr + 32 * i)),
-                                                            __builtin_bit_cast(bf16x8, vf[i]), dp, 0, 0, 0);
-            }
-            // rows of register v: query 32*qb + 8*(v/4) + 4*h + v%4, four at a time
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * qb + 8 * g + 4 * h);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * qb + 8 * g + 4 * h);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int v = 4 * g + e;
-                    float pr = fast_exp2(fmaf(s[v], p.c_log2, -l4[e]));
-                    if (masked && CAUSAL && my_k > m0 + 32 * qb + acc_row(v, h)) pr = 0.0f;
-                    pv[16 * qb + v] = pr;
-                    dsv[16 * qb + v] = pr * (dp[v] - d4[e]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int v = 4 * g + e;
+                float pr = fast_exp2(fmaf(s[v], p.c_log2, -l4[e]));
+                if (masked && CAUSAL && rel > 8 * g + e) pr = 0.0f;
+                pv[v] = pr;
+                dsv[v] = pr * (dp[v] - d4[e]);
             }
         }
-        bf16x8 pf[BQ / 16], dsf[BQ / 16];
+        bf16x8 pf[2], dsf[2];
 #pragma unroll
-        for (int cc = 0; cc < BQ / 16; ++cc)
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 pf[cc][e] = static_cast<__bf16>(pv[8 * cc + e]);
@@ -458,28 +455,37 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int cc = 0; cc < BQ / 16; ++cc) {
+            for (int cc = 0; cc < 2; ++cc) {
+                const int col = 32 * (2 * qb + cc);
                 dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, ld16(gtr + 32 * db * C::TROW + 32 * cc)), pf[cc], dv[db], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, ld16(gtr + 32 * db * C::TROW + col)), pf[cc], dv[db], 0, 0, 0);
                 dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, ld16(qtr + 32 * db * C::TROW + 32 * cc)), dsf[cc], dk[db], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, ld16(qtr + 32 * db * C::TROW + col)), dsf[cc], dk[db], 0, 0, 0);
             }
+    };
+    auto compute_block = [&](int t, int qb) {
+        if (t < t_first) return;
+        // a causal mask is needed while the tile starts before this wave's last key
+        compute(t, qb, CAUSAL && t * BQ < kw0 + 31);
     };
 
     if (t0 < n_qt) {
-        load_tile(t0);
-        store_tile(t0);
+        load_part(t0, 0);
+        store_part(t0, 0);
+        load_part(t0, 1);
+        store_part(t0, 1);
     }
     __syncthreads();
     for (int t = t0; t < n_qt; ++t) {
-        if (t + 1 < n_qt) load_tile(t + 1);
-        if (t >= t_first) {
-            // a causal mask is needed while the tile starts before this wave's last key
-            const int m0 = t * BQ;
-            if (CAUSAL && m0 < kw0 + 31) compute(t, true);
-            else compute(t, false);
+        const bool more = t + 1 < n_qt;
+        if (more) load_part(t + 1, 0);
+        compute_block(t, 0);
+        if (more) {
+            store_part(t + 1, 0);
+            load_part(t + 1, 1);
         }
-        if (t + 1 < n_qt) store_tile(t + 1);
+        compute_block(t, 1);
+        if (more) store_part(t + 1, 1);
         __syncthreads();
     }
 
