@@ -28,6 +28,9 @@ Modules:
 * ``fp8`` -- the OCP e4m3fn codec and the per-64-row-tile dynamic scaling.
 * ``online`` -- the pages' block-by-block online-softmax recurrences, used
   only to cross-check the two-pass definition.
+* ``splitkv`` -- attention restricted to a key range (a partial result with
+  its own lse) and the lse-weighted merge of partial results over disjoint
+  key ranges (ring attention's combination step, split-KV on one device).
 * ``backward`` -- dQ, dK, dV of the forward definition for an upstream
   gradient dO (the chain rule through scores, softmax and the product with
   V), in full and for sampled query rows or key columns.
@@ -36,10 +39,12 @@ from .attention import attention, attention_fp8, scores_rows
 from .fp8 import decode_e4m3, encode_e4m3, quantize_tiles, E4M3_MAX, TILE_ROWS
 from .online import online_softmax_attention, online_softmax_eager
 from .backward import attention_backward, dq_rows, dkdv_cols
+from .splitkv import attention_partial, merge_partials, split_ranges
 
 __all__ = [
     "attention", "attention_fp8", "scores_rows",
     "decode_e4m3", "encode_e4m3", "quantize_tiles", "E4M3_MAX", "TILE_ROWS",
     "online_softmax_attention", "online_softmax_eager",
     "attention_backward", "dq_rows", "dkdv_cols",
+    "attention_partial", "merge_partials", "split_ranges",
 ]
