@@ -9,7 +9,11 @@ and the float64 CPU oracle timed on a bounded sample of the same workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4_bf16]
                     [--no-cpu-baseline] [--no-bwd] [--calib-copy-mib M]
 
-The line also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
+The line also carries a ``splitkv`` object: ``fa_fwd`` against
+``fa_fwd_splitkv`` (keys split into ranges run as separate workgroups, then
+merged by lse) on the workload's per-device share at eight devices (H/8
+heads), where one query tile per workgroup no longer fills the device.
+It also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
 seeded upstream gradient) timed the same way on the same bf16 workload,
 with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
 matrix-core FLOPs the kernels actually execute (3.5 x: the dQ kernel
@@ -92,6 +96,44 @@ def cpu_baseline(w, q, k, v, budget_s: float):
             "sample": f"{done} query rows (every {stride}th row of {heads} head(s), all {w.N} keys each, "
                       f"float64 numpy) in {dt:.1f} s; TFLOP/s counted like the GPU figure, pro rata per row",
             "seconds": round(dt, 2), "cpu_model": _cpu_model()}
+
+
+def _time_calls(fn, steps: int, warmup: int = 3) -> np.ndarray:
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+
+
+def bench_splitkv(w, steps: int):
+    """fa_fwd vs fa_fwd_splitkv on the per-device share at eight devices (H/8 heads)."""
+    import torch
+    from tiled_attention_13_amd import fwd, fwd_splitkv
+    from tiled_attention_13_amd.inputs import make_inputs
+    shape = (w.B, w.H // 8, w.N, w.d)
+    q, k, v = (torch.from_numpy(a).to("cuda").to(torch.bfloat16) for a in make_inputs(w, shape=shape))
+    flops = w.flops() / 8
+    o = torch.empty_like(q)
+    lse = torch.empty(shape[:3], dtype=torch.float32, device="cuda")
+    base = float(_time_calls(lambda: fwd(q, k, v, causal=w.causal, out=o, lse=lse), steps).mean())
+    res = {"shape": list(shape), "fa_fwd_ms": round(base, 4), "fa_fwd_tflops": round(flops / base / 1e9, 2),
+           "splits": {}}
+    best = None
+    for n in (2, 4, 8):
+        ms = float(_time_calls(lambda: fwd_splitkv(q, k, v, n, causal=w.causal, out=o, lse=lse), steps).mean())
+        res["splits"][str(n)] = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 2)}
+        best = ms if best is None else min(best, ms)
+    res["best_speedup"] = round(base / best, 3)
+    return res
 
 
 def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
@@ -231,6 +273,8 @@ def main():
         "input_sha256": digest(q, k, v)[:16],
         "input_gen_s": round(gen_s, 2),
     }
+    if w.dtype == "bf16" and w.H % 8 == 0:
+        result["splitkv"] = bench_splitkv(w, args.steps)
     if not args.no_bwd and w.dtype == "bf16":
         result["backward"] = bench_backward(w, dq, dk, dv, out, lse, args.steps, args.warmup)
     if not args.no_cpu_baseline:

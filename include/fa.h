@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
     FA_F32 = 0,       /* q, k, v, o float32; products and softmax in fp32 */
@@ -126,6 +126,52 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
                      const void* v_bf16, void* o_bf16, float* lse,
                      int64_t B, int64_t H, int64_t N, int64_t d,
                      int causal, float softmax_scale, void* stream);
+
+/*
+ * fa_fwd_partial -- attention of every query over one key range only (bf16),
+ * the per-shard step of ring attention ("Flash Attention" tag page,
+ * excerpts on attention variants and on ring attention: the sequence is
+ * split over devices, each computes local attention and partial results are
+ * passed on and combined).
+ *   q, k, v : bf16 [B,H,N,d].  Keys [kv_begin, kv_end) are used, at their
+ *             positions in the sequence (the causal mask compares them with
+ *             the query positions 0..N-1 as they are).
+ *   kv_begin: multiple of 64;  kv_end: multiple of 64 or N;
+ *             0 <= kv_begin <= kv_end <= N (else FA_ERR_INVALID_ARGUMENT).
+ *   o_part  : float32 [B,H,N,d] output: O normalised over the visible keys of
+ *             the range (0 for a row that sees none of them).
+ *   lse_part: float32 [B,H,N] output: ln of the range's softmax denominator
+ *             (-inf for a row that sees none of its keys).
+ * Allocates a stream-ordered V^T workspace like fa_fwd.
+ */
+fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int64_t kv_begin, int64_t kv_end,
+                         int causal, float softmax_scale, void* stream);
+
+/*
+ * fa_merge -- combine n_parts partial results over disjoint key ranges.
+ *   o_parts : float32 [n_parts, B,H,N,d];  lse_parts : float32 [n_parts, B,H,N]
+ *             (as written by fa_fwd_partial; 1 <= n_parts <= 1024).
+ *   o       : bf16 output [B,H,N,d];  lse : float32 [B,H,N] output or NULL.
+ * With M = max_g lse_g:  lse = M + ln sum_g exp(lse_g - M),
+ *                        O   = sum_g exp(lse_g - lse) O_g
+ * (a row whose parts are all -inf gets O = 0 and lse = -inf).  Allocates
+ * nothing.
+ */
+fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d, void* stream);
+
+/*
+ * fa_fwd_splitkv -- fa_fwd for bf16 with the keys of every (b, h) split into
+ * n_splits ranges of whole 64-key tiles that run as separate workgroups,
+ * then merged as by fa_merge (1 <= n_splits <= 1024).  Same result as
+ * fa_fwd up to rounding; it fills the device when B*H*ceil(N/256) is small.
+ * Allocates one stream-ordered workspace: V^T plus n_splits float32 partial
+ * O and lse (n_splits*B*H*N*(d+1)*4 bytes).
+ */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
+                         int64_t n_splits, void* stream);
 
 /*
  * fa_bwd -- gradient of fa_fwd (FA_BF16 only).

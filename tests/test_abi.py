@@ -124,3 +124,31 @@ def test_fa_bwd_rejects_bad_arguments(lib):
     assert call(7, ptrs[6]) == 7                        # dk aliases dq
     assert call(6, ptrs[6] + 8) == 6                    # misaligned dq
     assert call(5, ptrs[5] + 2) == 6                    # misaligned lse
+
+
+def test_partial_merge_splitkv_reject_bad_arguments(lib):
+    P = FAKE
+    q, k, v, o, l = P, P + 0x1000, P + 0x2000, P + 0x3000, P + 0x4000
+    fp = lib.fa_fwd_partial
+    assert fp(q, k, v, o, 0, 1, 1, 128, 64, 0, 64, 0, 0.1, None) == 1          # lse_part NULL
+    assert fp(q, k, v, o, l, 1, 1, 128, 48, 0, 64, 0, 0.1, None) == 3
+    assert fp(q, k, v, o, l, 1, 1, 128, 64, 0, 64, 0, 0.0, None) == 4
+    assert fp(q, k, v, o, l, 1, 1, 128, 64, 32, 64, 0, 0.1, None) == 7        # kv_begin not tile aligned
+    assert fp(q, k, v, o, l, 1, 1, 128, 64, 0, 100, 0, 0.1, None) == 7        # kv_end neither aligned nor N
+    assert fp(q, k, v, o, l, 1, 1, 128, 64, 64, 0, 0, 0.1, None) == 7         # begin > end
+    assert fp(q, k, v, o, l, 1, 1, 128, 64, 0, 192, 0, 0.1, None) == 7        # end > N
+    assert fp(q, k, v, q, l, 1, 1, 128, 64, 0, 64, 0, 0.1, None) == 7         # o_part aliases q
+    assert fp(q, k, v, o + 4, l, 1, 1, 128, 64, 0, 64, 0, 0.1, None) == 6
+    m = lib.fa_merge
+    assert m(0, l, 2, o, None, 1, 1, 128, 64, None) == 1
+    assert m(q, l, 0, o, None, 1, 1, 128, 64, None) == 7
+    assert m(q, l, 1025, o, None, 1, 1, 128, 64, None) == 7
+    assert m(q, l, 2, q, None, 1, 1, 128, 64, None) == 7
+    assert m(q, l, 2, o, None, 1, 1, 128, 96, None) == 3
+    assert m(q + 8, l, 2, o, None, 1, 1, 128, 64, None) == 6
+    sk = lib.fa_fwd_splitkv
+    assert sk(q, k, v, 0, None, 1, 1, 128, 64, 0, 0.1, 2, None) == 1
+    assert sk(q, k, v, o, None, 1, 1, 128, 64, 0, 0.1, 0, None) == 7
+    assert sk(q, k, v, o, None, 1, 1, 128, 64, 2, 0.1, 2, None) == 7
+    assert sk(q, k, v, o, None, 1, 1, 128, 64, 0, -1.0, 2, None) == 4
+    assert sk(q, k, v, o, l + 2, 1, 1, 128, 64, 0, 0.1, 2, None) == 6

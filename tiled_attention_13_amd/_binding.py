@@ -23,6 +23,9 @@ SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_quant_fp8_e4m3": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _P]),
+    "fa_fwd_partial": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _F, _P]),
+    "fa_merge": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I64, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_abi_version": (_I, []),
@@ -178,3 +181,57 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, softmax_scale: float | None
                        B, H, N, d, int(bool(causal)), scale, FA_BF16, _stream_ptr(stream))
     _check(st, "fa_bwd")
     return dq, dk, dv
+
+
+def fwd_partial(q, k, v, kv_begin: int, kv_end: int, causal: bool = False, softmax_scale: float | None = None,
+                o_part=None, lse_part=None, stream=None):
+    """Attention over keys [kv_begin, kv_end) only (``fa_fwd_partial``), bf16 in.
+
+    Returns ``(o_part float32 [B,H,N,d], lse_part float32 [B,H,N])``: O
+    normalised over the range's visible keys and the range's logsumexp
+    (-inf for rows that see none of them).
+    """
+    import torch
+    _check_qkv(q, k, v, torch.bfloat16)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    o_part = torch.empty(q.shape, dtype=torch.float32, device=q.device) if o_part is None else o_part
+    lse_part = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse_part is None else lse_part
+    st = load().fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, H, N, d,
+                               int(kv_begin), int(kv_end), int(bool(causal)), scale, _stream_ptr(stream))
+    _check(st, "fa_fwd_partial")
+    return o_part, lse_part
+
+
+def merge(o_parts, lse_parts, out=None, lse=None, with_lse: bool = True, stream=None):
+    """Combine partial results (``fa_merge``): ``o_parts`` float32 [G,B,H,N,d],
+    ``lse_parts`` float32 [G,B,H,N] -> (bf16 O [B,H,N,d], float32 lse [B,H,N])."""
+    import torch
+    if o_parts.dim() != 5 or o_parts.dtype != torch.float32 or not o_parts.is_contiguous() or not o_parts.is_cuda:
+        raise ValueError("o_parts must be a contiguous float32 device tensor [G, B, H, N, d]")
+    G, B, H, N, d = o_parts.shape
+    if lse_parts.dtype != torch.float32 or tuple(lse_parts.shape) != (G, B, H, N) or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be a contiguous float32 device tensor [G, B, H, N]")
+    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device) if out is None else out
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    st = load().fa_merge(_ptr(o_parts), _ptr(lse_parts), G, _ptr(out), _ptr(lse), B, H, N, d, _stream_ptr(stream))
+    _check(st, "fa_merge")
+    return out, lse
+
+
+def fwd_splitkv(q, k, v, n_splits: int, causal: bool = False, softmax_scale: float | None = None,
+                out=None, lse=None, with_lse: bool = True, stream=None):
+    """bf16 attention forward with the keys split into ``n_splits`` ranges run as
+    separate workgroups and merged (``fa_fwd_splitkv``).  Returns ``(o, lse)``."""
+    import torch
+    _check_qkv(q, k, v, torch.bfloat16)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                               int(bool(causal)), scale, int(n_splits), _stream_ptr(stream))
+    _check(st, "fa_fwd_splitkv")
+    return out, lse

@@ -18,6 +18,7 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
+constexpr int64_t kMaxParts = 1024;     // partial results per merge / splits per call
 // 0 = unknown, 1 = gfx950, 2 = other architecture
 std::atomic<int> g_arch_state[kMaxDevices];
 
@@ -190,6 +191,109 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
             e = fa::launch_fwd(a, s);
         }
     }
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return launch_status(e);
+    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int64_t kv_begin, int64_t kv_end,
+                         int causal, float softmax_scale, void* stream) {
+    if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    if (kv_begin < 0 || kv_begin > kv_end || kv_end > N || kv_begin % fa::kKeyTile != 0 ||
+        (kv_end % fa::kKeyTile != 0 && kv_end != N))
+        return FA_ERR_INVALID_ARGUMENT;
+    const void* outs[] = {o_part, lse_part};
+    for (const void* x : outs)
+        if (x == q || x == k || x == v) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o_part, 16) || !aligned(lse_part, 4))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    void* vt = nullptr;
+    if (hipMallocAsync(&vt, vt_bytes(BH, n, dd), s) != hipSuccess || vt == nullptr) {
+        (void)hipGetLastError();
+        return FA_ERR_OUT_OF_MEMORY;
+    }
+    hipError_t e = fa::launch_transpose_v(v, vt, BH, n, dd, s);
+    if (e == hipSuccess) {
+        fa::FwdArgs a{fa::Kind::BF16, q, k, v, vt, nullptr, nullptr, nullptr, nullptr,
+                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+        a.o32 = o_part;
+        a.lse_part = lse_part;
+        a.kt_lo = static_cast<int>(kv_begin / fa::kKeyTile);
+        a.kt_hi = static_cast<int>((kv_end + fa::kKeyTile - 1) / fa::kKeyTile);
+        a.tps = a.kt_hi > a.kt_lo ? a.kt_hi - a.kt_lo : 1;
+        a.n_splits = 1;
+        e = fa::launch_fwd(a, s);
+    }
+    const hipError_t ef = hipFreeAsync(vt, s);
+    if (e != hipSuccess) return launch_status(e);
+    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t N, int64_t d, void* stream) {
+    if (!o_parts || !lse_parts || !o) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if (n_parts < 1 || n_parts > kMaxParts) return FA_ERR_INVALID_ARGUMENT;
+    if (o == o_parts || o == lse_parts || lse == o_parts || lse == lse_parts) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(o_parts, 16) || !aligned(o, 16) || !aligned(lse_parts, 4) || (lse && !aligned(lse, 4)))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    return launch_status(fa::launch_merge(o_parts, lse_parts, static_cast<int>(n_parts), o, lse,
+                                          static_cast<int>(B * H), static_cast<int>(N), static_cast<int>(d),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
+                         int64_t n_splits, void* stream) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    if (n_splits < 1 || n_splits > kMaxParts) return FA_ERR_INVALID_ARGUMENT;
+    if (o == q || o == k || o == v) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    const int n_tiles = (n + fa::kKeyTile - 1) / fa::kKeyTile;
+    const int tps = (n_tiles + static_cast<int>(n_splits) - 1) / static_cast<int>(n_splits);
+    const size_t rows = static_cast<size_t>(BH) * n;
+    const size_t off_o32 = round_up(vt_bytes(BH, n, dd), 256);
+    const size_t off_lse = off_o32 + round_up(static_cast<size_t>(n_splits) * rows * dd * 4, 256);
+    const size_t total = off_lse + round_up(static_cast<size_t>(n_splits) * rows * 4, 256);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return FA_ERR_OUT_OF_MEMORY;
+    }
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    float* o32 = reinterpret_cast<float*>(base + off_o32);
+    float* lse_part = reinterpret_cast<float*>(base + off_lse);
+    hipError_t e = fa::launch_transpose_v(v, base, BH, n, dd, s);
+    if (e == hipSuccess) {
+        fa::FwdArgs a{fa::Kind::BF16, q, k, v, base, nullptr, nullptr, nullptr, nullptr,
+                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+        a.o32 = o32;
+        a.lse_part = lse_part;
+        a.kt_lo = 0;
+        a.kt_hi = n_tiles;
+        a.tps = tps;
+        a.n_splits = static_cast<int>(n_splits);
+        e = fa::launch_fwd(a, s);
+    }
+    if (e == hipSuccess) e = fa::launch_merge(o32, lse_part, static_cast<int>(n_splits), o, lse, BH, n, dd, s);
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launch_status(e);
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;

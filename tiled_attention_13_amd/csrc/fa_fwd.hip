@@ -56,6 +56,12 @@ struct KParams {
     int np;
     int n_qtiles;
     float c_log2;       // softmax_scale * log2(e)
+    // partial results over key ranges (PARTIAL kernels only)
+    float* o32;         // [n_splits, BH, N, D] normalised over the split's keys
+    float* lse_part;    // [n_splits, BH, N], -inf where the split has no visible key
+    int kt_lo, kt_hi;   // key tiles [kt_lo, kt_hi) of the launch
+    int tps;            // key tiles per split
+    int n_splits;
 };
 
 // ---------------------------------------------------------------------------
@@ -138,7 +144,7 @@ struct PPCfg {
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
 
-template <int D, bool CAUSAL, bool FP8>
+template <int D, bool CAUSAL, bool FP8, bool PARTIAL>
 __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     using C = PPCfg<D, CAUSAL, FP8>;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, ES = C::ES;
@@ -152,6 +158,11 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
 
     int qt = blockIdx.x / p.BH;
     const int bh = blockIdx.x - qt * p.BH;
+    int split = 0;
+    if (PARTIAL) {
+        split = qt / p.n_qtiles;
+        qt -= split * p.n_qtiles;
+    }
     if (CAUSAL) qt = p.n_qtiles - 1 - qt;        // heaviest query tiles first
     const int q0 = qt * BM;
     const int qw0 = q0 + 32 * w;
@@ -186,16 +197,38 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     float c_q = p.c_log2;
     if (FP8) c_q = p.c_log2 / p.q_scale[bh * n_scale + (qw0 < N ? qw0 : N - 1) / 64];
 
+    // key tiles [lo, lo + n_kt) of this workgroup; tiles are counted from lo below
     const int n_all = (N + BN - 1) / BN;
-    const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
+    int lo = 0, hi = n_all;
+    if (PARTIAL) {
+        lo = p.kt_lo + split * p.tps;
+        hi = min(p.kt_hi, lo + p.tps);
+    }
+    if (CAUSAL) hi = min(hi, (min(q0 + BM, N) + BN - 1) / BN);
+    const int n_kt = hi - lo;
     // last key tile with any key at or before this wave's last query
-    const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
+    // (negative when a key range lies entirely after this wave's queries)
+    const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN - lo) : n_kt - 1;
+
+    if (PARTIAL && n_kt <= 0) {                   // no key of the range is visible to any query here
+        if (my_q < N) {
+            const size_t row = (static_cast<size_t>(split) * p.BH + bh) * N + my_q;
+            float* orow = p.o32 + row * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * h) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (h == 0) p.lse_part[row] = kNegInf;
+        }
+        return;
+    }
 
     // ---- global -> register staging of this thread's share of one K/V tile
     u32x4 kst[C::K_PER_T];
     u32x4 vst[C::V_PER_T];
     auto load_tile = [&](int t) {
-        const int n0 = t * BN;
+        const int n0 = (lo + t) * BN;
         const uint8_t* kt = kg + static_cast<size_t>(n0) * D * ES;
         const uint8_t* vt = vtg + static_cast<size_t>(n0) * 2;
         if (n0 + BN <= N) {                        // full tile: no per-row guards
@@ -341,7 +374,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     };
     // softmax of tile j, rescale of O, probabilities packed to bf16
     auto op_softmax = [&](int j, bool masked) {
-        const int n0 = j * BN;
+        const int n0 = (lo + j) * BN;
         if (masked) {
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
@@ -352,7 +385,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
                 }
         }
         float c = c_q;
-        if (FP8) c = c_q / p.k_scale[bh * n_scale + j];     // BN = 64: tile j is scale tile j
+        if (FP8) c = c_q / p.k_scale[bh * n_scale + lo + j];     // BN = 64: tile j is scale tile j
         const float alpha = softmax_step(s, c, m_run, l_run);
         // with the lazy reference max, alpha is 1 for every lane on most tiles:
         // skip the 16*D/32 multiplies then (a wave-uniform branch)
@@ -388,34 +421,64 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     //      M_0 | V_0 M_1 | V_1 M_2 | ... | V_{n-1} M_n
     // Tiles before j_last need no mask (their last key precedes this wave's
     // first query, and only the last tile can hold keys >= N).
-    op_s(0);
-    lds_barrier();
-    for (int j = 0; j < j_last; ++j) {
-        op_softmax(j, false);
-        traffic(j);
+    if (PARTIAL && j_last < 0) {
+        // every key of the range comes after this wave's queries: it only
+        // publishes its share of the tiles, in the same slots as the others
         lds_barrier();
-        op_pv(j);
-        __builtin_amdgcn_sched_barrier(0);
-        op_s(j + 1);
+        for (int j = 0; j < n_kt; ++j) {
+            traffic(j);
+            lds_barrier();
+            lds_barrier();
+        }
+    } else {
+        op_s(0);
         lds_barrier();
-    }
-    {
-        const int n0 = j_last * BN;
-        op_softmax(j_last, (CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N);
-        traffic(j_last);
-        lds_barrier();
-        op_pv(j_last);
-        lds_barrier();
-    }
-    for (int j = j_last + 1; j < n_kt; ++j) {     // this wave is past the diagonal: traffic only
-        traffic(j);
-        lds_barrier();
-        lds_barrier();
+        for (int j = 0; j < j_last; ++j) {
+            op_softmax(j, false);
+            traffic(j);
+            lds_barrier();
+            op_pv(j);
+            __builtin_amdgcn_sched_barrier(0);
+            op_s(j + 1);
+            lds_barrier();
+        }
+        {
+            const int n0 = (lo + j_last) * BN;
+            op_softmax(j_last, (CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N);
+            traffic(j_last);
+            lds_barrier();
+            op_pv(j_last);
+            lds_barrier();
+        }
+        for (int j = j_last + 1; j < n_kt; ++j) { // this wave is past the diagonal: traffic only
+            traffic(j);
+            lds_barrier();
+            lds_barrier();
+        }
     }
     if (grp == 0) lds_barrier();                  // group A idles through the last slot
 
     // ---- epilogue
     const float l_tot = sum_halves(l_run);
+    if (PARTIAL) {
+        // O normalised over this split's keys, in fp32, and the split's lse (-inf if it saw no key)
+        if (my_q < N) {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            const size_t row = (static_cast<size_t>(split) * p.BH + bh) * N + my_q;
+            float* orow = p.o32 + row * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 out;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out[e] = o[db][4 * g + e] * inv;
+                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * h) = out;
+                }
+            if (h == 0) p.lse_part[row] = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * kLn2 : kNegInf;
+        }
+        return;
+    }
     if (my_q < N) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         uint8_t* orow = p.o + (slice + static_cast<size_t>(my_q) * D) * 2;
@@ -610,6 +673,45 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint8_t* __restr
 }
 
 // ===========================================================================
+// Merge of partial results over disjoint key ranges: with M = max_g lse_g,
+// lse = M + ln sum_g exp(lse_g - M) and O = sum_g exp(lse_g - lse) O_g (the
+// combination step of ring attention, on one device).  D/4 lanes per row,
+// four fp32 values of every part per lane.
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_parts, const float* __restrict__ lse_parts,
+                                                    int n_parts, uint8_t* __restrict__ o, float* __restrict__ lse,
+                                                    long long rows) {
+    constexpr int LPR = D / 4;
+    const long long row = (static_cast<long long>(blockIdx.x) * 256 + threadIdx.x) / LPR;
+    const int part = threadIdx.x % LPR;
+    if (row >= rows) return;
+    float m = kNegInf;
+    for (int g = 0; g < n_parts; ++g) m = fmaxf(m, lse_parts[g * rows + row]);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lse_out = kNegInf;
+    if (m != kNegInf) {
+        float wsum = 0.0f;
+        for (int g = 0; g < n_parts; ++g) {
+            const float wg = expf(lse_parts[g * rows + row] - m);     // 0 for an empty part
+            const f32x4 x = *reinterpret_cast<const f32x4*>(o_parts + (g * rows + row) * D + 4 * part);
+            wsum += wg;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(wg, x[e], acc[e]);
+        }
+        const float inv = 1.0f / wsum;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= inv;
+        lse_out = m + logf(wsum);
+    }
+    bf16x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(acc[e]);
+    *reinterpret_cast<bf16x4*>(o + (row * D + 4 * part) * 2) = out;
+    if (lse != nullptr && part == 0) lse[row] = lse_out;
+}
+
+// ===========================================================================
 // Per-64-row-tile e4m3fn quantisation (one workgroup per tile)
 // ===========================================================================
 
@@ -682,8 +784,17 @@ hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
     kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8>), dim3(static_cast<int>(grid)), dim3(PPCfg<D, CAUSAL, FP8>::NT),
-                       0, st, kp);
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8, false>), dim3(static_cast<int>(grid)),
+                       dim3(PPCfg<D, CAUSAL, FP8>::NT), 0, st, kp);
+    return hipGetLastError();
+}
+template <int D, bool CAUSAL>
+hipError_t launch_partial(KParams kp, int BH, hipStream_t st) {
+    kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, false>::BM - 1) / PPCfg<D, CAUSAL, false>::BM;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * BH * kp.n_splits;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, false, true>), dim3(static_cast<int>(grid)),
+                       dim3(PPCfg<D, CAUSAL, false>::NT), 0, st, kp);
     return hipGetLastError();
 }
 template <int D, bool CAUSAL>
@@ -698,6 +809,8 @@ hipError_t launch_f32(KParams kp, int BH, hipStream_t st) {
 template <int D>
 hipError_t dispatch_d(const FwdArgs& a, const KParams& kp, hipStream_t st) {
     const int BH = a.BH;
+    if (a.o32 != nullptr)
+        return a.causal ? launch_partial<D, true>(kp, BH, st) : launch_partial<D, false>(kp, BH, st);
     switch (a.kind) {
         case Kind::F32:
             return a.causal ? launch_f32<D, true>(kp, BH, st) : launch_f32<D, false>(kp, BH, st);
@@ -726,6 +839,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.N = a.N;
     kp.n_qtiles = 0;                       // set per kernel from its query-tile height
     kp.c_log2 = a.softmax_scale * kLog2e;
+    kp.o32 = a.o32;
+    kp.lse_part = a.lse_part;
+    kp.kt_lo = a.kt_lo;
+    kp.kt_hi = a.kt_hi;
+    kp.tps = a.tps;
+    kp.n_splits = a.n_splits;
+    if (a.o32 != nullptr && (a.kind != Kind::BF16 || a.n_splits < 1 || a.tps < 1)) return hipErrorInvalidValue;
     switch (a.d) {
         case 32: return dispatch_d<32>(a, kp, stream);
         case 64: return dispatch_d<64>(a, kp, stream);
@@ -745,6 +865,21 @@ hipError_t launch_transpose_v(const void* v, void* vt, int BH, int N, int d, hip
         case 32: hipLaunchKernelGGL(transpose_v_kernel<32>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
         case 64: hipLaunchKernelGGL(transpose_v_kernel<64>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
         case 128: hipLaunchKernelGGL(transpose_v_kernel<128>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+                        int BH, int N, int d, hipStream_t stream) {
+    const long long rows = static_cast<long long>(BH) * N;
+    const long long grid = (rows * (d / 4) + 255) / 256;
+    if (grid > 0x7FFFFFFFLL || n_parts < 1) return hipErrorInvalidConfiguration;
+    uint8_t* out = static_cast<uint8_t*>(o);
+    switch (d) {
+        case 32: hipLaunchKernelGGL(merge_kernel<32>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, o_parts, lse_parts, n_parts, out, lse, rows); break;
+        case 64: hipLaunchKernelGGL(merge_kernel<64>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, o_parts, lse_parts, n_parts, out, lse, rows); break;
+        case 128: hipLaunchKernelGGL(merge_kernel<128>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, o_parts, lse_parts, n_parts, out, lse, rows); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

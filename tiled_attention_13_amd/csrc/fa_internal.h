@@ -24,6 +24,14 @@ struct FwdArgs {
     int d;
     bool causal;
     float softmax_scale;
+    // Partial results (bf16 only): when o32 is set, the kernel computes, for
+    // each split s < n_splits, attention over key tiles
+    // [kt_lo + s*tps, min(kt_hi, kt_lo + (s+1)*tps)) and writes O normalised over
+    // those keys to o32 [n_splits, BH, N, d] (fp32) and its lse to lse_part
+    // [n_splits, BH, N] (-inf where no key is visible); o and lse are not written.
+    float* o32 = nullptr;
+    float* lse_part = nullptr;
+    int kt_lo = 0, kt_hi = 0, tps = 0, n_splits = 0;
 };
 
 // Enqueue the forward kernel on `stream`; returns the launch status.
@@ -31,6 +39,12 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 
 // Keys per tile of the bf16/FP8 attention kernel; V^T rows are padded to a multiple of it.
 constexpr int kKeyTile = 64;
+
+// Enqueue the merge of n_parts partial results (o_parts [n_parts, BH, N, d]
+// fp32, lse_parts [n_parts, BH, N]) into bf16 o [BH, N, d] and lse (may be null):
+// lse = ln sum_g exp(lse_g), O = sum_g exp(lse_g - lse) O_g.
+hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+                        int BH, int N, int d, hipStream_t stream);
 
 // Enqueue the transposition of a bf16 V [BH, N, d] into vt [BH, d, np] (np = N rounded
 // up to kKeyTile, padding zero), keys permuted within each tile into the order the
