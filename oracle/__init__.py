@@ -31,6 +31,8 @@ Modules:
 * ``splitkv`` -- attention restricted to a key range (a partial result with
   its own lse) and the lse-weighted merge of partial results over disjoint
   key ranges (ring attention's combination step, split-KV on one device).
+* ``blocksparse`` -- attention with a 64x64 block mask (only the blocks the
+  table allows are computed), optionally combined with the causal mask.
 * ``backward`` -- dQ, dK, dV of the forward definition for an upstream
   gradient dO (the chain rule through scores, softmax and the product with
   V), in full and for sampled query rows or key columns.
@@ -40,6 +42,7 @@ from .fp8 import decode_e4m3, encode_e4m3, quantize_tiles, E4M3_MAX, TILE_ROWS
 from .online import online_softmax_attention, online_softmax_eager
 from .backward import attention_backward, dq_rows, dkdv_cols
 from .splitkv import attention_partial, merge_partials, split_ranges
+from .blocksparse import attention_blocksparse, expand_block_mask, visible_pairs
 
 __all__ = [
     "attention", "attention_fp8", "scores_rows",
@@ -47,4 +50,5 @@ __all__ = [
     "online_softmax_attention", "online_softmax_eager",
     "attention_backward", "dq_rows", "dkdv_cols",
     "attention_partial", "merge_partials", "split_ranges",
+    "attention_blocksparse", "expand_block_mask", "visible_pairs",
 ]
