@@ -13,6 +13,10 @@ The line also carries a ``splitkv`` object: ``fa_fwd`` against
 ``fa_fwd_splitkv`` (keys split into ranges run as separate workgroups, then
 merged by lse) on the workload's per-device share at eight devices (H/8
 heads), where one query tile per workgroup no longer fills the device.
+A ``blocksparse`` object times ``fa_fwd_blocksparse`` on the same workload
+with a sliding-window (16 blocks) plus global (2 blocks) table of 64x64
+blocks, TFLOP/s counted over the (query, key) pairs the table and the causal
+mask leave visible.
 It also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
 seeded upstream gradient) timed the same way on the same bf16 workload,
 with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
@@ -134,6 +138,35 @@ def bench_splitkv(w, steps: int):
         best = ms if best is None else min(best, ms)
     res["best_speedup"] = round(base / best, 3)
     return res
+
+
+def blocksparse_pairs(mask: np.ndarray, N: int, causal: bool) -> int:
+    """Visible (query, key) pairs of a 64x64 block table, by block arithmetic."""
+    nb = mask.shape[0]
+    sizes = np.minimum(64, N - 64 * np.arange(nb))
+    full = np.outer(sizes, sizes)
+    if causal:
+        full = np.where(np.arange(nb)[:, None] > np.arange(nb)[None, :], full, 0)
+        diag = sizes * (sizes + 1) // 2
+        full = full + np.diag(diag)
+    return int((full * (mask != 0)).sum())
+
+
+def bench_blocksparse(w, tq, tk, tv, steps: int):
+    import torch
+    from tiled_attention_13_amd import fwd_blocksparse
+    from tiled_attention_13_amd.inputs import band_global_block_mask
+    nb = (w.N + 63) // 64
+    mask = band_global_block_mask(nb)
+    tm = torch.from_numpy(mask).to("cuda")
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    ms = float(_time_calls(lambda: fwd_blocksparse(tq, tk, tv, tm, causal=w.causal, out=o, lse=lse), steps).mean())
+    flops = 4.0 * w.d * w.B * w.H * blocksparse_pairs(mask, w.N, w.causal)
+    kept = int(np.tril(mask).sum()) if w.causal else int(mask.sum())
+    total = nb * (nb + 1) // 2 if w.causal else nb * nb
+    return {"table": "sliding window 16 blocks + 2 global blocks (64x64)", "blocks_kept": kept,
+            "blocks_total": total, "ms_per_call": round(ms, 4), "tflops_visible": round(flops / ms / 1e9, 2)}
 
 
 def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
@@ -275,6 +308,8 @@ def main():
     }
     if w.dtype == "bf16" and w.H % 8 == 0:
         result["splitkv"] = bench_splitkv(w, args.steps)
+    if w.dtype == "bf16":
+        result["blocksparse"] = bench_blocksparse(w, dq, dk, dv, args.steps)
     if not args.no_bwd and w.dtype == "bf16":
         result["backward"] = bench_backward(w, dq, dk, dv, out, lse, args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
     FA_F32 = 0,       /* q, k, v, o float32; products and softmax in fp32 */
@@ -172,6 +172,26 @@ fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
                          int64_t n_splits, void* stream);
+
+/*
+ * fa_fwd_blocksparse -- bf16 attention where only the blocks a 0/1 table
+ * allows are computed ("Flash Attention" tag page, excerpt on attention
+ * variants: block sparse attention cuts the attention matrix into blocks
+ * and computes only some of them).
+ *   q, k, v, o, lse : as fa_fwd with FA_BF16 (lse may be NULL).
+ *   block_mask : device bytes; with nb = ceil(N/64), key j is visible to
+ *             query i iff block_mask[(b*H + h)*mask_bh_stride + (i/64)*nb + j/64]
+ *             != 0 (and j <= i when causal = 1).
+ *   mask_bh_stride : 0 (one nb x nb table for every (b, h)) or nb*nb (one
+ *             table per (b, h)); anything else is FA_ERR_INVALID_ARGUMENT.
+ * A row that sees no key gets O = 0 and lse = -inf.  Key tiles that no
+ * query of a 256-row tile may see are never loaded.  Allocates one
+ * stream-ordered workspace: V^T plus the per-tile visit lists
+ * (B*H*ceil(N/256)*(nb+1)*4 bytes).
+ */
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t d, const uint8_t* block_mask,
+                             int64_t mask_bh_stride, int causal, float softmax_scale, void* stream);
 
 /*
  * fa_bwd -- gradient of fa_fwd (FA_BF16 only).

@@ -152,3 +152,16 @@ def test_partial_merge_splitkv_reject_bad_arguments(lib):
     assert sk(q, k, v, o, None, 1, 1, 128, 64, 2, 0.1, 2, None) == 7
     assert sk(q, k, v, o, None, 1, 1, 128, 64, 0, -1.0, 2, None) == 4
     assert sk(q, k, v, o, l + 2, 1, 1, 128, 64, 0, 0.1, 2, None) == 6
+
+
+def test_blocksparse_rejects_bad_arguments(lib):
+    P = FAKE
+    q, k, v, o, m = P, P + 0x1000, P + 0x2000, P + 0x3000, P + 0x4000
+    f = lib.fa_fwd_blocksparse
+    assert f(q, k, v, o, None, 1, 1, 128, 64, 0, 0, 0, 0.1, None) == 1           # mask NULL
+    assert f(q, k, v, o, None, 1, 1, 128, 64, m, 3, 0, 0.1, None) == 7           # stride neither 0 nor nb*nb
+    assert f(q, k, v, o, None, 1, 1, 128, 64, m, 0, 2, 0.1, None) == 7
+    assert f(q, k, v, m, None, 1, 1, 128, 64, m, 0, 0, 0.1, None) == 7           # o aliases the mask
+    assert f(q, k, v, o, None, 1, 1, 128, 40, m, 4, 0, 0.1, None) == 3
+    assert f(q, k, v, o, None, 1, 1, 128, 64, m, 4, 0, float("inf"), None) == 4
+    assert f(q, k, v, o + 8, None, 1, 1, 128, 64, m, 4, 0, 0.1, None) == 6

@@ -70,3 +70,14 @@ def test_flop_and_byte_calculator_against_page_arithmetic():
     assert WORKLOADS["c4_bf16"].compulsory_bytes() == 538_968_064
     assert WORKLOADS["c5_fp8"].compulsory_bytes() == 404_815_872
     assert WORKLOADS["c1_f32"].compulsory_bytes() == 263_168
+
+
+def test_bench_blocksparse_pair_count_matches_oracle():
+    import bench
+    import oracle
+    from tiled_attention_13_amd.inputs import band_global_block_mask, random_block_mask
+    for N in (64, 100, 300, 1000):
+        nb = (N + 63) // 64
+        for m in (band_global_block_mask(nb, 3, 1), random_block_mask(nb, 0.5, N), np.ones((nb, nb), np.uint8)):
+            for causal in (False, True):
+                assert bench.blocksparse_pairs(m, N, causal) == oracle.visible_pairs(m, N, causal)

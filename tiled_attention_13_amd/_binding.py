@@ -26,6 +26,7 @@ SIGNATURES = {
     "fa_fwd_partial": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _F, _P]),
     "fa_merge": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I64, _P]),
+    "fa_fwd_blocksparse": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _I, _F, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
     "fa_abi_version": (_I, []),
@@ -234,4 +235,34 @@ def fwd_splitkv(q, k, v, n_splits: int, causal: bool = False, softmax_scale: flo
     st = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                int(bool(causal)), scale, int(n_splits), _stream_ptr(stream))
     _check(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, softmax_scale: float | None = None,
+                    out=None, lse=None, with_lse: bool = True, stream=None):
+    """bf16 attention with a 64x64 block table (``fa_fwd_blocksparse``).
+
+    ``block_mask``: uint8 device tensor ``[nb, nb]`` (shared by all heads) or
+    ``[B, H, nb, nb]``, nb = ceil(N/64); nonzero = the block is computed.
+    Returns ``(o, lse)``; rows that see no key get O = 0 and lse = -inf.
+    """
+    import torch
+    _check_qkv(q, k, v, torch.bfloat16)
+    B, H, N, d = q.shape
+    nb = (N + 63) // 64
+    if block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 device tensor")
+    if tuple(block_mask.shape) == (nb, nb):
+        stride = 0
+    elif tuple(block_mask.shape) == (B, H, nb, nb):
+        stride = nb * nb
+    else:
+        raise ValueError(f"block_mask must be [{nb}, {nb}] or [{B}, {H}, {nb}, {nb}]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and with_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, _ptr(block_mask),
+                                   stride, int(bool(causal)), scale, _stream_ptr(stream))
+    _check(st, "fa_fwd_blocksparse")
     return out, lse

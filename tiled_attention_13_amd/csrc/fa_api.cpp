@@ -299,6 +299,49 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t d, const uint8_t* block_mask,
+                             int64_t mask_bh_stride, int causal, float softmax_scale, void* stream) {
+    if (!q || !k || !v || !o || !block_mask) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    const int64_t nb = (N + fa::kKeyTile - 1) / fa::kKeyTile;
+    if (mask_bh_stride != 0 && mask_bh_stride != nb * nb) return FA_ERR_INVALID_ARGUMENT;
+    if (o == q || o == k || o == v || o == block_mask) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+        return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    const size_t n_lists = static_cast<size_t>(BH) * ((n + fa::kQueryTile - 1) / fa::kQueryTile);
+    const size_t off_list = round_up(vt_bytes(BH, n, dd), 256);
+    const size_t off_cnt = off_list + round_up(n_lists * static_cast<size_t>(nb) * 4, 256);
+    const size_t total = off_cnt + round_up(n_lists * 4, 256);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
+        (void)hipGetLastError();
+        return FA_ERR_OUT_OF_MEMORY;
+    }
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    uint32_t* list = reinterpret_cast<uint32_t*>(base + off_list);
+    int* cnt = reinterpret_cast<int*>(base + off_cnt);
+    hipError_t e = fa::launch_transpose_v(v, base, BH, n, dd, s);
+    if (e == hipSuccess) e = fa::launch_bs_plan(block_mask, mask_bh_stride, BH, n, causal == 1, list, cnt, s);
+    if (e == hipSuccess) {
+        fa::FwdArgs a{fa::Kind::BF16, q, k, v, base, o, lse, nullptr, nullptr,
+                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+        a.bs_list = list;
+        a.bs_count = cnt;
+        a.bs_stride = static_cast<int>(nb);
+        e = fa::launch_fwd(a, s);
+    }
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e != hipSuccess) return launch_status(e);
+    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
                  int causal, float softmax_scale, fa_dtype dtype, void* stream) {

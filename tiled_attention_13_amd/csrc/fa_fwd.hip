@@ -62,7 +62,15 @@ struct KParams {
     int kt_lo, kt_hi;   // key tiles [kt_lo, kt_hi) of the launch
     int tps;            // key tiles per split
     int n_splits;
+    // block-sparse kernels: per (bh, query tile) the list of key tiles to visit,
+    // entry = tile | (bit b set if 64-query block b of the tile needs it) << 24
+    const uint32_t* bs_list;
+    const int* bs_count;
+    int bs_stride;
 };
+
+// kernel variants of fwd_pp_kernel
+enum : int { kModeDense = 0, kModePartial = 1, kModeSparse = 2 };
 
 // ---------------------------------------------------------------------------
 // Online-softmax step on the scores one lane holds for its query.
@@ -144,9 +152,10 @@ struct PPCfg {
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
 
-template <int D, bool CAUSAL, bool FP8, bool PARTIAL>
+template <int D, bool CAUSAL, bool FP8, int MODE>
 __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     using C = PPCfg<D, CAUSAL, FP8>;
+    constexpr bool PARTIAL = MODE == kModePartial, SPARSE = MODE == kModeSparse;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, ES = C::ES;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE];
 
@@ -205,11 +214,33 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         hi = min(p.kt_hi, lo + p.tps);
     }
     if (CAUSAL) hi = min(hi, (min(q0 + BM, N) + BN - 1) / BN);
+    const uint32_t* bs = nullptr;
+    if (SPARSE) {
+        bs = p.bs_list + static_cast<size_t>(bh * p.n_qtiles + qt) * p.bs_stride;
+        hi = p.bs_count[bh * p.n_qtiles + qt];
+    }
     const int n_kt = hi - lo;
+    // key tile of list position t, and whether this wave computes it
+    auto tile_of = [&](int t) -> int { return SPARSE ? static_cast<int>(bs[t] & 0xFFFFFFu) : lo + t; };
+    auto needs = [&](int t) -> bool {
+        return ((bs[t] >> (24 + (w >> 1))) & 1u) != 0 && !(CAUSAL && tile_of(t) * BN > qw0 + 31);
+    };
     // last key tile with any key at or before this wave's last query
     // (negative when a key range lies entirely after this wave's queries)
     const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN - lo) : n_kt - 1;
 
+    if (SPARSE && n_kt <= 0) {                    // the block table leaves these queries no key
+        if (my_q < N) {
+            uint8_t* orow = p.o + (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<u32x2*>(orow + 2 * (32 * db + 8 * g + 4 * h)) = u32x2{0u, 0u};
+            if (p.lse != nullptr && h == 0) p.lse[static_cast<size_t>(bh) * N + my_q] = kNegInf;
+        }
+        return;
+    }
     if (PARTIAL && n_kt <= 0) {                   // no key of the range is visible to any query here
         if (my_q < N) {
             const size_t row = (static_cast<size_t>(split) * p.BH + bh) * N + my_q;
@@ -228,7 +259,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     u32x4 kst[C::K_PER_T];
     u32x4 vst[C::V_PER_T];
     auto load_tile = [&](int t) {
-        const int n0 = (lo + t) * BN;
+        const int n0 = tile_of(t) * BN;
         const uint8_t* kt = kg + static_cast<size_t>(n0) * D * ES;
         const uint8_t* vt = vtg + static_cast<size_t>(n0) * 2;
         if (n0 + BN <= N) {                        // full tile: no per-row guards
@@ -374,7 +405,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     };
     // softmax of tile j, rescale of O, probabilities packed to bf16
     auto op_softmax = [&](int j, bool masked) {
-        const int n0 = (lo + j) * BN;
+        const int n0 = tile_of(j) * BN;
         if (masked) {
 #pragma unroll
             for (int kb = 0; kb < BN / 32; ++kb)
@@ -385,7 +416,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
                 }
         }
         float c = c_q;
-        if (FP8) c = c_q / p.k_scale[bh * n_scale + lo + j];     // BN = 64: tile j is scale tile j
+        if (FP8) c = c_q / p.k_scale[bh * n_scale + tile_of(j)];     // BN = 64: tile j is scale tile j
         const float alpha = softmax_step(s, c, m_run, l_run);
         // with the lazy reference max, alpha is 1 for every lane on most tiles:
         // skip the 16*D/32 multiplies then (a wave-uniform branch)
@@ -421,7 +452,23 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     //      M_0 | V_0 M_1 | V_1 M_2 | ... | V_{n-1} M_n
     // Tiles before j_last need no mask (their last key precedes this wave's
     // first query, and only the last tile can hold keys >= N).
-    if (PARTIAL && j_last < 0) {
+    if (SPARSE) {
+        // the same slots over the listed tiles; a wave skips the work of a tile
+        // its 64-query block does not need (or that lies above its diagonal)
+        if (needs(0)) op_s(0);
+        lds_barrier();
+        for (int j = 0; j < n_kt; ++j) {
+            const bool nj = needs(j);
+            const int n0 = tile_of(j) * BN;
+            if (nj) op_softmax(j, (CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N);
+            traffic(j);
+            lds_barrier();
+            if (nj) op_pv(j);
+            __builtin_amdgcn_sched_barrier(0);
+            if (j + 1 < n_kt && needs(j + 1)) op_s(j + 1);
+            lds_barrier();
+        }
+    } else if (PARTIAL && j_last < 0) {
         // every key of the range comes after this wave's queries: it only
         // publishes its share of the tiles, in the same slots as the others
         lds_barrier();
@@ -784,7 +831,7 @@ hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
     kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8, false>), dim3(static_cast<int>(grid)),
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8, kModeDense>), dim3(static_cast<int>(grid)),
                        dim3(PPCfg<D, CAUSAL, FP8>::NT), 0, st, kp);
     return hipGetLastError();
 }
@@ -793,9 +840,43 @@ hipError_t launch_partial(KParams kp, int BH, hipStream_t st) {
     kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, false>::BM - 1) / PPCfg<D, CAUSAL, false>::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH * kp.n_splits;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, false, true>), dim3(static_cast<int>(grid)),
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, false, kModePartial>), dim3(static_cast<int>(grid)),
                        dim3(PPCfg<D, CAUSAL, false>::NT), 0, st, kp);
     return hipGetLastError();
+}
+template <int D, bool CAUSAL>
+hipError_t launch_sparse(KParams kp, int BH, hipStream_t st) {
+    static_assert(PPCfg<D, CAUSAL, false>::BM == kQueryTile, "visit lists are planned per 256-query tile");
+    kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, false>::BM - 1) / PPCfg<D, CAUSAL, false>::BM;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, false, kModeSparse>), dim3(static_cast<int>(grid)),
+                       dim3(PPCfg<D, CAUSAL, false>::NT), 0, st, kp);
+    return hipGetLastError();
+}
+
+// Visit lists of the block-sparse kernel: one thread per (bh, 256-query tile)
+// walks the key tiles and keeps those that one of its four 64-query blocks
+// may see (table entry set, and at or below the diagonal when causal).
+__global__ __launch_bounds__(256) void bs_plan_kernel(const uint8_t* __restrict__ mask, long long mask_bh_stride,
+                                                      int BH, int n_qtiles, int nb, bool causal,
+                                                      uint32_t* __restrict__ list, int* __restrict__ count) {
+    const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+    if (idx >= static_cast<long long>(BH) * n_qtiles) return;
+    const int bh = static_cast<int>(idx / n_qtiles), qt = static_cast<int>(idx - static_cast<long long>(bh) * n_qtiles);
+    const uint8_t* mb = mask + static_cast<size_t>(bh) * mask_bh_stride;
+    uint32_t* out = list + static_cast<size_t>(idx) * nb;
+    int cnt = 0;
+    for (int kb = 0; kb < nb; ++kb) {
+        uint32_t flags = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int qb = 4 * qt + b;
+            if (qb < nb && mb[static_cast<size_t>(qb) * nb + kb] != 0 && (!causal || kb <= qb)) flags |= 1u << b;
+        }
+        if (flags != 0) out[cnt++] = static_cast<uint32_t>(kb) | (flags << 24);
+    }
+    count[idx] = cnt;
 }
 template <int D, bool CAUSAL>
 hipError_t launch_f32(KParams kp, int BH, hipStream_t st) {
@@ -811,6 +892,8 @@ hipError_t dispatch_d(const FwdArgs& a, const KParams& kp, hipStream_t st) {
     const int BH = a.BH;
     if (a.o32 != nullptr)
         return a.causal ? launch_partial<D, true>(kp, BH, st) : launch_partial<D, false>(kp, BH, st);
+    if (a.bs_list != nullptr)
+        return a.causal ? launch_sparse<D, true>(kp, BH, st) : launch_sparse<D, false>(kp, BH, st);
     switch (a.kind) {
         case Kind::F32:
             return a.causal ? launch_f32<D, true>(kp, BH, st) : launch_f32<D, false>(kp, BH, st);
@@ -845,7 +928,11 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.kt_hi = a.kt_hi;
     kp.tps = a.tps;
     kp.n_splits = a.n_splits;
+    kp.bs_list = a.bs_list;
+    kp.bs_count = a.bs_count;
+    kp.bs_stride = a.bs_stride;
     if (a.o32 != nullptr && (a.kind != Kind::BF16 || a.n_splits < 1 || a.tps < 1)) return hipErrorInvalidValue;
+    if (a.bs_list != nullptr && (a.kind != Kind::BF16 || a.o32 != nullptr)) return hipErrorInvalidValue;
     switch (a.d) {
         case 32: return dispatch_d<32>(a, kp, stream);
         case 64: return dispatch_d<64>(a, kp, stream);
@@ -867,6 +954,18 @@ hipError_t launch_transpose_v(const void* v, void* vt, int BH, int N, int d, hip
         case 128: hipLaunchKernelGGL(transpose_v_kernel<128>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, dst, N, np, n_tiles); break;
         default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_bs_plan(const uint8_t* mask, long long mask_bh_stride, int BH, int N, bool causal,
+                          uint32_t* list, int* count, hipStream_t stream) {
+    const int nb = (N + kKeyTile - 1) / kKeyTile;
+    const int n_qtiles = (N + 255) / 256;
+    const long long threads = static_cast<long long>(BH) * n_qtiles;
+    const long long grid = (threads + 255) / 256;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bs_plan_kernel, dim3(static_cast<int>(grid)), dim3(256), 0, stream, mask, mask_bh_stride, BH,
+                       n_qtiles, nb, causal, list, count);
     return hipGetLastError();
 }
 

@@ -32,7 +32,22 @@ struct FwdArgs {
     float* o32 = nullptr;
     float* lse_part = nullptr;
     int kt_lo = 0, kt_hi = 0, tps = 0, n_splits = 0;
+    // Block-sparse (bf16 only): when bs_list is set, each (bh, 256-query tile)
+    // visits only the key tiles listed by launch_bs_plan.
+    const uint32_t* bs_list = nullptr;
+    const int* bs_count = nullptr;
+    int bs_stride = 0;
 };
+
+// Query rows per workgroup of the bf16/FP8 attention kernel (four 64-row blocks).
+constexpr int kQueryTile = 256;
+
+// Enqueue the planning pass of the block-sparse kernel: for every (bh, 256-query
+// tile) the key tiles any of its four 64-query blocks may see under the 0/1
+// table mask[bh * mask_bh_stride + qb * nb + kb] (nb = ceil(N/64); causal drops
+// kb > qb).  list holds BH * ceil(N/256) * nb entries, count BH * ceil(N/256).
+hipError_t launch_bs_plan(const uint8_t* mask, long long mask_bh_stride, int BH, int N, bool causal,
+                          uint32_t* list, int* count, hipStream_t stream);
 
 // Enqueue the forward kernel on `stream`; returns the launch status.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);

@@ -150,3 +150,21 @@ def make_grad(w: Workload, seed: int | None = None, shape: tuple | None = None):
     shp = tuple(shape) if shape is not None else w.shape
     rng = np.random.Generator(np.random.PCG64((w.seed if seed is None else seed) + 1_000_003))
     return round_to_bf16(rng.standard_normal(shp, dtype=np.float32))
+
+
+def band_global_block_mask(nb: int, window: int = 16, n_global: int = 2) -> np.ndarray:
+    """0/1 table [nb, nb] of 64x64 blocks: every query block sees the ``window``
+    key blocks ending at its own (a sliding window) plus the first ``n_global``
+    key blocks (global tokens) -- the sliding-window-plus-global pattern the
+    pages cite for sparse attention.  Blocks above the diagonal are left to the
+    causal flag."""
+    qb = np.arange(nb)[:, None]
+    kb = np.arange(nb)[None, :]
+    m = ((kb <= qb) & (kb > qb - window)) | (kb < n_global)
+    return m.astype(np.uint8)
+
+
+def random_block_mask(nb: int, density: float, seed: int, shape_prefix: tuple = ()) -> np.ndarray:
+    """Seeded 0/1 block table with about ``density`` of the blocks set."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.random(tuple(shape_prefix) + (nb, nb)) < density).astype(np.uint8)
