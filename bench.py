@@ -7,7 +7,7 @@ halved for causal), ms per call, the roofline entry of the attention kernel
 and the float64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4_bf16]
-                    [--no-cpu-baseline] [--no-bwd] [--calib-copy-mib M]
+                    [--no-cpu-baseline] [--no-bwd] [--headline-only] [--calib-copy-mib M]
 
 The line also carries a ``splitkv`` object: ``fa_fwd`` against
 ``fa_fwd_splitkv`` (keys split into ranges run as separate workgroups, then
@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0)
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the headline fa_fwd (no split-KV, block-sparse or backward objects)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -306,11 +308,12 @@ def main():
         "input_sha256": digest(q, k, v)[:16],
         "input_gen_s": round(gen_s, 2),
     }
-    if w.dtype == "bf16" and w.H % 8 == 0:
+    extras = not args.headline_only and w.dtype == "bf16"
+    if extras and w.H % 8 == 0:
         result["splitkv"] = bench_splitkv(w, args.steps)
-    if w.dtype == "bf16":
+    if extras:
         result["blocksparse"] = bench_blocksparse(w, dq, dk, dv, args.steps)
-    if not args.no_bwd and w.dtype == "bf16":
+    if extras and not args.no_bwd:
         result["backward"] = bench_backward(w, dq, dk, dv, out, lse, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_seconds)
