@@ -25,7 +25,8 @@ Modules:
 
 * ``attention`` -- the definition: scores materialised in float64, explicit
   causal mask, two-pass softmax, ``O = P V`` and the per-row logsumexp.
-* ``fp8`` -- the OCP e4m3fn codec and the per-64-row-tile dynamic scaling.
+* ``fp8`` -- the OCP e4m3fn codec, the per-64-row-tile dynamic scaling of Q
+  and K, and the power-of-two per-(tile, column) scaling of V for FP8 P*V.
 * ``online`` -- the pages' block-by-block online-softmax recurrences, used
   only to cross-check the two-pass definition.
 * ``splitkv`` -- attention restricted to a key range (a partial result with
@@ -38,7 +39,8 @@ Modules:
   V), in full and for sampled query rows or key columns.
 """
 from .attention import attention, attention_fp8, scores_rows
-from .fp8 import decode_e4m3, encode_e4m3, quantize_tiles, E4M3_MAX, TILE_ROWS
+from .fp8 import (decode_e4m3, encode_e4m3, quantize_tiles, E4M3_MAX, TILE_ROWS, pow2_exponent,
+                  quantize_v_pow2, dequantize_v_pow2)
 from .online import online_softmax_attention, online_softmax_eager
 from .backward import attention_backward, dq_rows, dkdv_cols
 from .splitkv import attention_partial, merge_partials, split_ranges
@@ -47,6 +49,7 @@ from .blocksparse import attention_blocksparse, expand_block_mask, visible_pairs
 __all__ = [
     "attention", "attention_fp8", "scores_rows",
     "decode_e4m3", "encode_e4m3", "quantize_tiles", "E4M3_MAX", "TILE_ROWS",
+    "pow2_exponent", "quantize_v_pow2", "dequantize_v_pow2",
     "online_softmax_attention", "online_softmax_eager",
     "attention_backward", "dq_rows", "dkdv_cols",
     "attention_partial", "merge_partials", "split_ranges",

@@ -90,3 +90,60 @@ def quantize_tiles(x, tile_rows: int = TILE_ROWS):
                 codes[b, h, t * tile_rows:(t + 1) * tile_rows] = encode_e4m3(y)
                 scale[b, h, t] = s
     return codes, scale
+
+
+# ---------------------------------------------------------------------------
+# Power-of-two scaled e4m3 for the P*V product.  The pages give the dynamic
+# per-block scale only for K (and by the same reading Q); for an FP8 P*V they
+# name FP8 without details (tag page, excerpt on V3).  The reading taken here
+# keeps every scale a power of two, so that scaling is exact and the product's
+# dequantisation is the matrix core's own per-block exponent:
+#
+#   V: for each (b, h), 64-key tile t and column c,
+#        e = the largest integer with amax * 2**e <= 448 (amax = max |V| over
+#            the tile's keys in column c; e = 0 for an all-zero column),
+#        code = e4m3fn(V * 2**e)          (exact scaling, then nearest-even),
+#        value = decode(code) * 2**-e.
+#   P: each probability tile of one query is scaled the same way from its
+#      largest entry inside the kernel; that rounding is not reproduced here
+#      (the parity tolerance accounts for it).
+# ---------------------------------------------------------------------------
+
+def pow2_exponent(amax) -> np.ndarray:
+    """Largest integer e with amax * 2**e <= 448 (0 where amax == 0), elementwise.
+
+    Exact: amax = m * 2**x with m in [0.5, 1) and 448 = 0.875 * 2**9, so
+    e = 9 - x when m <= 0.875 and 8 - x otherwise.
+    """
+    a = np.asarray(amax, dtype=np.float64)
+    m, x = np.frexp(a)
+    e = np.where(m <= 0.875, 9 - x, 8 - x)
+    return np.where(a == 0.0, 0, e).astype(np.int64)
+
+
+def quantize_v_pow2(v, tile_rows: int = TILE_ROWS):
+    """Power-of-two e4m3 quantisation of ``v [B, H, N, d]`` per (64-key tile, column).
+
+    Returns ``(codes uint8 [B,H,N,d], exps int64 [B,H,ceil(N/tile_rows),d])``;
+    ``decode_e4m3(codes) * 2**-exps`` (tile-broadcast) gives the values used.
+    """
+    v = np.asarray(v, dtype=np.float32).astype(np.float64)
+    B, H, N, d = v.shape
+    n_tiles = (N + tile_rows - 1) // tile_rows
+    codes = np.empty((B, H, N, d), dtype=np.uint8)
+    exps = np.empty((B, H, n_tiles, d), dtype=np.int64)
+    for t in range(n_tiles):
+        rows = slice(t * tile_rows, min(N, (t + 1) * tile_rows))
+        amax = np.abs(v[:, :, rows]).max(axis=2)               # [B, H, d]
+        e = pow2_exponent(amax)
+        exps[:, :, t] = e
+        codes[:, :, rows] = encode_e4m3(np.ldexp(v[:, :, rows], e[:, :, None, :]))
+    return codes, exps
+
+
+def dequantize_v_pow2(codes, exps, tile_rows: int = TILE_ROWS) -> np.ndarray:
+    """Values ``decode(code) * 2**-e`` of a power-of-two quantised V (float64)."""
+    vals = decode_e4m3(codes)
+    N = vals.shape[2]
+    e_rows = np.repeat(np.asarray(exps), tile_rows, axis=2)[:, :, :N]
+    return np.ldexp(vals, -e_rows)

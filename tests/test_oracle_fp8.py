@@ -125,3 +125,49 @@ def test_fp8_attention_equals_attention_on_dequantised_values():
         # quantisation perturbs the result only slightly relative to the unquantised inputs
         O_raw, _ = oracle.attention(q, k, v, causal, 0.25)
         assert np.max(np.abs(O - O_raw)) < 0.1
+
+
+# ---------------------------------------------------------------------------
+# power-of-two scaled V (FP8 P*V)
+# ---------------------------------------------------------------------------
+
+def test_pow2_exponent_definition():
+    cases = {448.0: 0, 448.00001: -1, 447.9: 0, 224.0: 1, 224.0001: 0, 1.0: 8, 0.875: 9, 0.8751: 8,
+             3.5: 7, 3.50001: 6, 2.0 ** -20: 28, 1e30: -91, 0.0: 0}
+    for a, e in cases.items():
+        assert oracle.pow2_exponent(a) == e, (a, e)
+    rng = np.random.default_rng(5)
+    a = np.exp(rng.uniform(-40, 40, 100000))
+    e = oracle.pow2_exponent(a)
+    assert np.all(np.ldexp(a, e) <= 448.0) and np.all(np.ldexp(a, e + 1) > 448.0)
+
+
+def test_quantize_v_pow2_properties():
+    rng = np.random.default_rng(6)
+    v = (rng.standard_normal((2, 3, 150, 16)) * np.exp(rng.uniform(-6, 6, (2, 3, 1, 16)))).astype(np.float32)
+    v[0, 0, 64:128, 3] = 0.0                                  # an all-zero column of a tile
+    codes, exps = oracle.quantize_v_pow2(v)
+    assert codes.shape == v.shape and exps.shape == (2, 3, 3, 16)
+    assert exps[0, 0, 1, 3] == 0 and np.all(codes[0, 0, 64:128, 3] == 0)
+    vals = oracle.dequantize_v_pow2(codes, exps)
+    # each value is within half an e4m3 step of V: relative 2^-4 for normals,
+    # absolute 2^-10 * 2^-e in the subnormal range
+    e_rows = np.repeat(exps, 64, axis=2)[:, :, :150]
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, np.ldexp(2.0 ** -10, -e_rows))
+    assert np.all(np.abs(vals - v) <= bound * (1 + 1e-12))
+    # the largest magnitude of every (tile, column) lands in (224, 448]
+    for t in range(3):
+        top = np.abs(decode_e4m3(codes[:, :, 64 * t:64 * t + 64])).max(axis=2)
+        nz = np.abs(v[:, :, 64 * t:64 * t + 64]).max(axis=2) > 0
+        assert np.all(top[nz] > 224 * (1 - 2.0 ** -4)) and np.all(top[nz] <= 448)
+
+
+def test_quantize_v_pow2_matches_torch_cast():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((1, 2, 200, 32)).astype(np.float32) * 3
+    codes, exps = oracle.quantize_v_pow2(v)
+    e_rows = np.repeat(exps, 64, axis=2)[:, :, :200]
+    scaled = np.ldexp(v.astype(np.float64), e_rows).astype(np.float32)   # exact: powers of two
+    ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes, ref)
