@@ -43,7 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS & % MFMA peak (bf16 causal N=16K d=128); ms/call"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp8pv": 5000.0, "f32": 157.3}   # MI355X dense MFMA peaks
 PEAK_HBM_GBPS = 8000.0
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_13_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_bf16_traffic.json")
@@ -167,6 +167,24 @@ def bench_blocksparse(w, tq, tk, tv, steps: int):
     total = nb * (nb + 1) // 2 if w.causal else nb * nb
     return {"table": "sliding window 16 blocks + 2 global blocks (64x64)", "blocks_kept": kept,
             "blocks_total": total, "ms_per_call": round(ms, 4), "tflops_visible": round(flops / ms / 1e9, 2)}
+
+
+def bench_fp8(steps: int):
+    """The FP8 workload (1x16x32768x128 causal) with Q/K on e4m3 (bf16 P*V) and with P*V on e4m3 too."""
+    import torch
+    from tiled_attention_13_amd import fwd
+    from tiled_attention_13_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["c5_fp8"]
+    q, k, v = (torch.from_numpy(a).to("cuda").to(torch.bfloat16) for a in make_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    res = {"shape": list(w.shape), "causal": w.causal}
+    for dt in ("fp8", "fp8pv"):
+        ms = float(_time_calls(lambda: fwd(q, k, v, causal=w.causal, dtype=dt, out=o, lse=lse), steps).mean())
+        res[dt] = {"ms_per_call": round(ms, 4), "tflops": round(w.flops() / ms / 1e9, 2),
+                   "pct_fp8_peak": round(100.0 * w.flops() / ms / 1e9 / PEAK_TFLOPS["fp8"], 2)}
+    res["note"] = "fp8: Q.K^T on e4m3, P.V on bf16; fp8pv: both on e4m3; quantisation pre-passes included"
+    return res
 
 
 def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
@@ -313,6 +331,8 @@ def main():
         result["splitkv"] = bench_splitkv(w, args.steps)
     if extras:
         result["blocksparse"] = bench_blocksparse(w, dq, dk, dv, args.steps)
+    if extras:
+        result["fp8"] = bench_fp8(args.steps)
     if extras and not args.no_bwd:
         result["backward"] = bench_backward(w, dq, dk, dv, out, lse, args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -54,14 +54,20 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
     FA_F32 = 0,       /* q, k, v, o float32; products and softmax in fp32 */
     FA_BF16 = 1,      /* q, k, v, o bfloat16; fp32 accumulation */
-    FA_FP8_E4M3 = 2   /* q, k, v, o bfloat16 on input; Q and K quantised to
+    FA_FP8_E4M3 = 2,  /* q, k, v, o bfloat16 on input; Q and K quantised to
                          e4m3fn per 64-row tile inside the call (see
                          fa_quant_fp8_e4m3), V and P*V stay bf16 */
+    FA_FP8_E4M3_PV = 3 /* as FA_FP8_E4M3, and P*V also on e4m3 matrix cores:
+                         V quantised per (64-key tile, column) with a
+                         power-of-two scale (see fa_quant_v_pow2), P per
+                         (query, 64-key tile) with a power-of-two scale
+                         inside the kernel; both scales are the MFMA's own
+                         block exponents, so dequantisation is exact */
 } fa_dtype;
 
 typedef enum {
@@ -87,7 +93,8 @@ typedef enum {
  *   causal  : 0 or 1.
  *   softmax_scale : finite and > 0; multiplies the fp32 scores (it is not
  *             folded into the stored Q).
- *   dtype   : FA_F32, FA_BF16 or FA_FP8_E4M3.  For FA_BF16 and
+ *   dtype   : FA_F32, FA_BF16, FA_FP8_E4M3 or FA_FP8_E4M3_PV (workspace:
+ *             e4m3 Q, K, V^T and their scales).  For FA_BF16 and
  *             FA_FP8_E4M3 the call allocates one stream-ordered workspace
  *             (hipMallocAsync / hipFreeAsync on `stream`) for V transposed
  *             (B*H*d*ceil(N/64)*64 bf16) and, for FA_FP8_E4M3, the quantised
@@ -113,6 +120,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  */
 fa_status fa_quant_fp8_e4m3(const void* x_bf16, uint8_t* x8, float* scale,
                             int64_t BH, int64_t N, int64_t d, void* stream);
+
+/*
+ * fa_quant_v_pow2 -- the V pre-pass of FA_FP8_E4M3_PV (tag page, excerpt on
+ * V3: FP8 for the products; the power-of-two scale is this library's reading).
+ *   v_bf16  : input bf16 [BH, N, d].
+ *   v8      : output e4m3fn codes [BH, d, np] with np = ceil(N/64)*64: V
+ *             transposed, the 64 keys of each tile stored in the order the
+ *             attention kernel's P operand meets them, padding codes 0.
+ *   v_scale : output bytes [BH, ceil(N/64), d]: 127 - e, where e is the
+ *             largest integer (clipped to [-127, 127]; 0 for an all-zero
+ *             column) with max|V| over the tile's keys in that column * 2^e
+ *             <= 448.  code = e4m3fn_RNE(V * 2^e); V ~= decode(code) * 2^-e.
+ */
+fa_status fa_quant_v_pow2(const void* v_bf16, uint8_t* v8, uint8_t* v_scale, int64_t BH, int64_t N, int64_t d,
+                          void* stream);
 
 /*
  * fa_fwd_fp8 -- attention forward on already-quantised Q and K.

@@ -110,7 +110,8 @@ def quantize_tiles(x, tile_rows: int = TILE_ROWS):
 # ---------------------------------------------------------------------------
 
 def pow2_exponent(amax) -> np.ndarray:
-    """Largest integer e with amax * 2**e <= 448 (0 where amax == 0), elementwise.
+    """Largest integer e with amax * 2**e <= 448 (0 where amax == 0), clipped to
+    [-127, 127] (the range of an 8-bit block exponent), elementwise.
 
     Exact: amax = m * 2**x with m in [0.5, 1) and 448 = 0.875 * 2**9, so
     e = 9 - x when m <= 0.875 and 8 - x otherwise.
@@ -118,7 +119,7 @@ def pow2_exponent(amax) -> np.ndarray:
     a = np.asarray(amax, dtype=np.float64)
     m, x = np.frexp(a)
     e = np.where(m <= 0.875, 9 - x, 8 - x)
-    return np.where(a == 0.0, 0, e).astype(np.int64)
+    return np.clip(np.where(a == 0.0, 0, e), -127, 127).astype(np.int64)
 
 
 def quantize_v_pow2(v, tile_rows: int = TILE_ROWS):

@@ -66,7 +66,7 @@ def _fwd(lib, **over):
     (dict(B=1 << 20, H=1 << 10, N=1 << 10, d=64), 2),
     (dict(d=48), 3), (dict(d=256), 3), (dict(d=16), 3),
     (dict(scale=0.0), 4), (dict(scale=-1.0), 4), (dict(scale=float("inf")), 4), (dict(scale=float("nan")), 4),
-    (dict(dtype=3), 5), (dict(dtype=-1), 5),
+    (dict(dtype=4), 5), (dict(dtype=-1), 5),
     (dict(causal=2), 7), (dict(o=FAKE), 7),
     (dict(q=FAKE + 8), 6), (dict(o=FAKE + 0x3004), 6), (dict(lse=FAKE + 0x4002), 6),
 ])
@@ -165,3 +165,13 @@ def test_blocksparse_rejects_bad_arguments(lib):
     assert f(q, k, v, o, None, 1, 1, 128, 40, m, 4, 0, 0.1, None) == 3
     assert f(q, k, v, o, None, 1, 1, 128, 64, m, 4, 0, float("inf"), None) == 4
     assert f(q, k, v, o + 8, None, 1, 1, 128, 64, m, 4, 0, 0.1, None) == 6
+
+
+def test_quant_v_pow2_rejects_bad_arguments(lib):
+    P = FAKE
+    q = lib.fa_quant_v_pow2
+    assert q(0, P, P, 1, 64, 64, None) == 1
+    assert q(P, P, 0, 1, 64, 64, None) == 1
+    assert q(P, P, P, 0, 64, 64, None) == 2
+    assert q(P, P, P, 1, 64, 48, None) == 3
+    assert q(P + 2, P, P, 1, 64, 64, None) == 6

@@ -133,11 +133,12 @@ def test_fp8_attention_equals_attention_on_dequantised_values():
 
 def test_pow2_exponent_definition():
     cases = {448.0: 0, 448.00001: -1, 447.9: 0, 224.0: 1, 224.0001: 0, 1.0: 8, 0.875: 9, 0.8751: 8,
-             3.5: 7, 3.50001: 6, 2.0 ** -20: 28, 1e30: -91, 0.0: 0}
+             3.5: 7, 3.50001: 6, 2.0 ** -20: 28, 1e30: -91, 0.0: 0, 1e-39: 127, 2.0 ** -118: 126,
+             2.0 ** -119: 127, 1e300: -127}
     for a, e in cases.items():
         assert oracle.pow2_exponent(a) == e, (a, e)
     rng = np.random.default_rng(5)
-    a = np.exp(rng.uniform(-40, 40, 100000))
+    a = np.exp(rng.uniform(-40, 40, 100000))      # well inside the clip range
     e = oracle.pow2_exponent(a)
     assert np.all(np.ldexp(a, e) <= 448.0) and np.all(np.ldexp(a, e + 1) > 448.0)
 

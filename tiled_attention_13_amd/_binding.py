@@ -14,14 +14,15 @@ import os
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 _lib = None
 
-FA_F32, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
-DTYPE_CODES = {"f32": FA_F32, "bf16": FA_BF16, "fp8": FA_FP8_E4M3}
+FA_F32, FA_BF16, FA_FP8_E4M3, FA_FP8_E4M3_PV = 0, 1, 2, 3
+DTYPE_CODES = {"f32": FA_F32, "bf16": FA_BF16, "fp8": FA_FP8_E4M3, "fp8pv": FA_FP8_E4M3_PV}
 
 # (name, restype, argtypes) of every entry point declared in include/fa.h
 _P, _I64, _I, _F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_quant_fp8_e4m3": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "fa_quant_v_pow2": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "fa_fwd_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _P]),
     "fa_fwd_partial": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _F, _P]),
     "fa_merge": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]),
@@ -95,8 +96,9 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None, dtype
     """Fused attention forward through ``fa_fwd``.
 
     q, k, v: contiguous device tensors ``[B, H, N, d]`` (float32 for
-    dtype "f32", bfloat16 for "bf16" and "fp8"; "fp8" quantises Q and K to
-    e4m3 per 64-row tile inside the call).  ``softmax_scale`` defaults to
+    dtype "f32", bfloat16 for "bf16", "fp8" and "fp8pv"; "fp8" quantises Q
+    and K to e4m3 per 64-row tile inside the call, "fp8pv" also V, and runs
+    P*V on e4m3 as well).  ``softmax_scale`` defaults to
     ``1/sqrt(d)``.  Returns ``(o, lse)`` (lse is None when ``with_lse`` is
     False and no ``lse`` buffer is given).
     """
@@ -266,3 +268,20 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, softmax_scale: fl
                                    stride, int(bool(causal)), scale, _stream_ptr(stream))
     _check(st, "fa_fwd_blocksparse")
     return out, lse
+
+
+def quant_v_pow2(v, stream=None):
+    """Power-of-two e4m3 quantisation of a bf16 V ``[B, H, N, d]`` (``fa_quant_v_pow2``).
+
+    Returns ``(codes uint8 [B,H,d,np] (tile-permuted keys), scale_bytes uint8 [B,H,ceil(N/64),d])``.
+    """
+    import torch
+    if not v.is_cuda or v.dtype != torch.bfloat16 or not v.is_contiguous() or v.dim() != 4:
+        raise ValueError("v must be a contiguous bf16 device tensor [B, H, N, d]")
+    B, H, N, d = v.shape
+    np_ = (N + 63) // 64 * 64
+    codes = torch.empty((B, H, d, np_), dtype=torch.uint8, device=v.device)
+    sc = torch.empty((B, H, (N + 63) // 64, d), dtype=torch.uint8, device=v.device)
+    st = load().fa_quant_v_pow2(_ptr(v), _ptr(codes), _ptr(sc), B * H, N, d, _stream_ptr(stream))
+    _check(st, "fa_quant_v_pow2")
+    return codes, sc

@@ -138,7 +138,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     fa_status st = check_shape(B, H, N, d);
     if (st != FA_OK) return st;
     if ((st = check_scale(softmax_scale)) != FA_OK) return st;
-    if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_INVALID_DTYPE;
+    if (dtype != FA_F32 && dtype != FA_BF16 && dtype != FA_FP8_E4M3 && dtype != FA_FP8_E4M3_PV)
+        return FA_ERR_INVALID_DTYPE;
     if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
     if (o == q || o == k || o == v) return FA_ERR_INVALID_ARGUMENT;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
@@ -151,6 +152,44 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
         fa::FwdArgs a{fa::Kind::F32, q, k, v, nullptr, o, lse, nullptr, nullptr, BH, n, n, dd, causal == 1,
                       softmax_scale};
         return launch_status(fa::launch_fwd(a, s));
+    }
+
+    if (dtype == FA_FP8_E4M3_PV) {
+        // e4m3 Q and K (per-tile fp32 scales), e4m3 V^T (power-of-two block exponents)
+        const size_t codes = static_cast<size_t>(BH) * n * dd;
+        const size_t n_scales = static_cast<size_t>(BH) * ((n + 63) / 64);
+        const size_t v8b = static_cast<size_t>(BH) * dd * padded_keys(n);
+        const size_t off_v8 = 0;
+        const size_t off_vs = off_v8 + round_up(v8b, 256);
+        const size_t off_q8 = off_vs + round_up(n_scales * dd, 256);
+        const size_t off_k8 = off_q8 + round_up(codes, 256);
+        const size_t off_qs = off_k8 + round_up(codes, 256);
+        const size_t off_ks = off_qs + round_up(n_scales * 4, 256);
+        const size_t total = off_ks + round_up(n_scales * 4, 256);
+        void* ws = nullptr;
+        if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
+            (void)hipGetLastError();
+            return FA_ERR_OUT_OF_MEMORY;
+        }
+        uint8_t* base = static_cast<uint8_t*>(ws);
+        uint8_t* v8 = base + off_v8;
+        uint8_t* vs = base + off_vs;
+        uint8_t* q8 = base + off_q8;
+        uint8_t* k8 = base + off_k8;
+        float* qs = reinterpret_cast<float*>(base + off_qs);
+        float* ks = reinterpret_cast<float*>(base + off_ks);
+        hipError_t e = fa::launch_quant_v_pow2(v, v8, vs, BH, n, dd, s);
+        if (e == hipSuccess) e = fa::launch_quant_fp8(q, q8, qs, BH, n, dd, s);
+        if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, ks, BH, n, dd, s);
+        if (e == hipSuccess) {
+            fa::FwdArgs a{fa::Kind::FP8PV, q8, k8, v, v8, o, lse, qs, ks, BH, n, padded_keys(n), dd, causal == 1,
+                          softmax_scale};
+            a.v_scale = vs;
+            e = fa::launch_fwd(a, s);
+        }
+        const hipError_t ef = hipFreeAsync(ws, s);
+        if (e != hipSuccess) return launch_status(e);
+        return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
     }
 
     // bf16 / FP8: one stream-ordered workspace for V^T and, for FP8, the e4m3
@@ -340,6 +379,17 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e != hipSuccess) return launch_status(e);
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_quant_v_pow2(const void* v_bf16, uint8_t* v8, uint8_t* v_scale, int64_t BH, int64_t N, int64_t d,
+                          void* stream) {
+    if (!v_bf16 || !v8 || !v_scale) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(1, BH, N, d);
+    if (st != FA_OK) return st;
+    if (!aligned(v_bf16, 16) || !aligned(v8, 16)) return FA_ERR_MISALIGNED;
+    if ((st = check_device()) != FA_OK) return st;
+    return launch_status(fa::launch_quant_v_pow2(v_bf16, v8, v_scale, static_cast<int>(BH), static_cast<int>(N),
+                                                 static_cast<int>(d), static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

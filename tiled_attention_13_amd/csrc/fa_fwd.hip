@@ -67,6 +67,8 @@ struct KParams {
     const uint32_t* bs_list;
     const int* bs_count;
     int bs_stride;
+    // FP8 P*V: MFMA block-scale bytes (127 - e) of the e4m3 V^T, [BH, n_tiles, D]
+    const uint8_t* vscale;
 };
 
 // kernel variants of fwd_pp_kernel
@@ -109,6 +111,46 @@ __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m,
     return alpha;
 }
 
+// Same step for an e4m3 P*V product: the probabilities come out multiplied by
+// 2^f, with f the largest integer (at most 127) for which this tile's largest
+// probability stays within the e4m3 range 448 (so they fill that range before
+// rounding); 127 - f is the matrix core's block exponent that undoes it.  l
+// still sums the unscaled fp32 probabilities.
+template <int NS>
+__device__ __forceinline__ float softmax_step_p8(float (&s)[NS], float c, float& m, float& l, int& scale_b) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) mx = fmaxf(mx, s[i]);
+    const float mx2 = max_halves(mx) * c;
+    float alpha = 1.0f;
+    if (mx2 > m + kRescaleSlack) {
+        alpha = fast_exp2(m - mx2);
+        m = mx2;
+    }
+    const float m_use = (m == kNegInf) ? 0.0f : m;
+    // log2 of the tile's largest probability is mx2 - m_use; log2(448) = 8.807...
+    const float fl = floorf(8.807354922f - (mx2 - m_use));
+    const int f = fl > 126.0f ? 126 : (fl < -126.0f ? -126 : static_cast<int>(fl));   // -inf tile: 126
+    const float shift = static_cast<float>(f) - m_use;
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const float p = fast_exp2(fmaf(s[i], c, shift));
+        s[i] = p;
+        rs += p;
+    }
+    l = fmaf(rs, __int_as_float((127 - f) << 23), l * alpha);      // rs * 2^-f
+    scale_b = 127 - f;
+    return alpha;
+}
+
+// Byte position, inside a 64-key row of the e4m3 V^T, of key kk: the order in
+// which one lane's 32 P values (the two 32-key score blocks of its query, in
+// register order) meet the k-slots of the 32x32x64 e4m3 MFMA.
+__device__ __forceinline__ int f8_slot(int kk) {
+    return (((kk >> 2) & 1) << 5) | (((kk >> 5) & 1) << 4) | (((kk >> 3) & 3) << 2) | (kk & 3);
+}
+
 // ===========================================================================
 // bf16 / fp8 kernel, ping-pong schedule
 //
@@ -129,7 +171,7 @@ __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m,
 // slot 2t-3) is done by then, and A first reads tile t in slot 2t.  Global
 // loads land in registers two slots before they are written to LDS.
 // ===========================================================================
-template <int D, bool CAUSAL, bool FP8>
+template <int D, bool CAUSAL, bool FP8, bool PV8 = false>
 struct PPCfg {
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
@@ -138,23 +180,26 @@ struct PPCfg {
     static constexpr int STAGES = 3;
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
-    static constexpr int VROW = 2 * BN + 16;     // bytes per V^T row in LDS (padded)
+    static constexpr int VES = PV8 ? 1 : 2;      // bytes per V element
+    static constexpr int VROW = VES * BN + 16;   // bytes per V^T row in LDS (padded)
     static constexpr int KBYTES = BN * KROW;
     static constexpr int VBYTES = D * VROW;
-    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int SBYTES = PV8 ? (D + 15) / 16 * 16 : 0;   // V block exponents of the tile
+    static constexpr int STAGE = KBYTES + VBYTES + SBYTES;
     static constexpr int K_CPR = D * ES / 16;    // 16-byte chunks per K row
     static constexpr int K_CHUNKS = BN * K_CPR;
     static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-    static constexpr int V_CHUNKS = D * (2 * BN / 16);  // 16-byte chunks of a V^T tile (D rows x BN keys)
+    static constexpr int V_CPR = VES * BN / 16;  // 16-byte chunks per V^T row of a tile
+    static constexpr int V_CHUNKS = D * V_CPR;   // 16-byte chunks of a V^T tile (D rows x BN keys)
     static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
     static constexpr bool F8W = FP8 && (D % 64 == 0);
     static constexpr bool F8N = FP8 && !F8W;
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
 
-template <int D, bool CAUSAL, bool FP8, int MODE>
+template <int D, bool CAUSAL, bool FP8, int MODE, bool PV8 = false>
 __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
-    using C = PPCfg<D, CAUSAL, FP8>;
+    using C = PPCfg<D, CAUSAL, FP8, PV8>;
     constexpr bool PARTIAL = MODE == kModePartial, SPARSE = MODE == kModeSparse;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, ES = C::ES;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE];
@@ -181,7 +226,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     const uint8_t* qg = p.q + slice * ES;
     const uint8_t* kg = p.k + slice * ES;
     // V^T rows of this (b, h): D rows of np keys
-    const uint8_t* vtg = p.vt + static_cast<size_t>(bh) * D * p.np * 2;
+    const uint8_t* vtg = p.vt + static_cast<size_t>(bh) * D * p.np * C::VES;
 
     // ---- Q fragments (B operand of S^T = K Q^T)
     u32x4 qf[C::F8W ? 2 * C::QREGS : C::QREGS];
@@ -258,10 +303,16 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     // ---- global -> register staging of this thread's share of one K/V tile
     u32x4 kst[C::K_PER_T];
     u32x4 vst[C::V_PER_T];
+    u32x4 sst = {0, 0, 0, 0};                    // FP8 P*V: V block exponents of the tile
+    const int n_all_tiles = (N + BN - 1) / BN;
     auto load_tile = [&](int t) {
         const int n0 = tile_of(t) * BN;
         const uint8_t* kt = kg + static_cast<size_t>(n0) * D * ES;
-        const uint8_t* vt = vtg + static_cast<size_t>(n0) * 2;
+        const uint8_t* vt = vtg + static_cast<size_t>(n0) * C::VES;
+        if constexpr (PV8) {
+            if (tid < C::SBYTES / 16)
+                sst = ld16(p.vscale + (static_cast<size_t>(bh) * n_all_tiles + tile_of(t)) * D + 16 * tid);
+        }
         if (n0 + BN <= N) {                        // full tile: no per-row guards
 #pragma unroll
             for (int i = 0; i < C::K_PER_T; ++i) {
@@ -286,8 +337,8 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         for (int i = 0; i < C::V_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
-                const int d = c / (2 * BN / 16), col = c - d * (2 * BN / 16);
-                vst[i] = ld16(vt + static_cast<size_t>(d) * p.np * 2 + 16 * col);
+                const int d = c / C::V_CPR, col = c - d * C::V_CPR;
+                vst[i] = ld16(vt + static_cast<size_t>(d) * p.np * C::VES + 16 * col);
             }
         }
     };
@@ -306,9 +357,12 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         for (int i = 0; i < C::V_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
-                const int d = c / (2 * BN / 16), col = c - d * (2 * BN / 16);
+                const int d = c / C::V_CPR, col = c - d * C::V_CPR;
                 *reinterpret_cast<u32x4*>(vs + d * C::VROW + 16 * col) = vst[i];
             }
+        }
+        if constexpr (PV8) {
+            if (tid < C::SBYTES / 16) *reinterpret_cast<u32x4*>(vs + C::VBYTES + 16 * tid) = sst;
         }
     };
 
@@ -320,10 +374,12 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     float m_run = kNegInf, l_run = 0.0f;
     float s[BN / 2];
     bf16x8 pf[BN / 16];
+    uint32_t pf8[BN / 8];                        // FP8 P*V: the lane's 32 P values as e4m3 codes
+    int p_scale = 127;                           // FP8 P*V: block exponent of those codes
 
     // per-lane LDS addresses of this lane's K row / V^T row fragments in stage 0
     const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
-    const uint8_t* lane_v = smem + C::KBYTES + l32 * C::VROW + 16 * h;
+    const uint8_t* lane_v = smem + C::KBYTES + l32 * C::VROW + (PV8 ? 32 : 16) * h;
 
     // ---- the four ops of the schedule
     // S^T = K_j Q^T for tile j
@@ -389,6 +445,23 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     // O^T += V_j^T P^T for tile j
     auto op_pv = [&](int j) {
         const uint8_t* vl = lane_v + (j % C::STAGES) * C::STAGE;
+        if constexpr (PV8) {
+            // O^T += V^T P^T on the 32x32x64 e4m3 MFMA: one per 32 rows of d covers the
+            // whole 64-key tile; both operands carry their power-of-two block exponents
+            const uint8_t* sc = smem + (j % C::STAGES) * C::STAGE + C::KBYTES + C::VBYTES;
+            const i32x8 b = {(int)pf8[0], (int)pf8[1], (int)pf8[2], (int)pf8[3],
+                             (int)pf8[4], (int)pf8[5], (int)pf8[6], (int)pf8[7]};
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const u32x4 a0 = ld16(vl + 32 * db * C::VROW);
+                const u32x4 a1 = ld16(vl + 32 * db * C::VROW + 16);
+                const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                 (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                const int sa = sc[32 * db + l32];
+                o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, o[db], 0, 0, 0, sa, 0, p_scale);
+            }
+            return;
+        }
         constexpr int NA = (D / 32) * (BN / 16);
         bf16x8 a[NA];
 #pragma unroll
@@ -417,7 +490,9 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         }
         float c = c_q;
         if (FP8) c = c_q / p.k_scale[bh * n_scale + tile_of(j)];     // BN = 64: tile j is scale tile j
-        const float alpha = softmax_step(s, c, m_run, l_run);
+        float alpha;
+        if constexpr (PV8) alpha = softmax_step_p8(s, c, m_run, l_run, p_scale);
+        else alpha = softmax_step(s, c, m_run, l_run);
         // with the lazy reference max, alpha is 1 for every lane on most tiles:
         // skip the 16*D/32 multiplies then (a wave-uniform branch)
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
@@ -426,10 +501,20 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
         }
+        if constexpr (PV8) {
+            // byte t of the B operand is s[t] (register order = the k-slot order of f8_slot)
 #pragma unroll
-        for (int cc = 0; cc < BN / 16; ++cc)
+            for (int wd = 0; wd < BN / 8; ++wd) {
+                int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[4 * wd], s[4 * wd + 1], 0, false);
+                x = __builtin_amdgcn_cvt_pk_fp8_f32(s[4 * wd + 2], s[4 * wd + 3], x, true);
+                pf8[wd] = static_cast<uint32_t>(x);
+            }
+        } else {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) pf[cc][t] = static_cast<__bf16>(s[8 * cc + t]);
+            for (int cc = 0; cc < BN / 16; ++cc)
+#pragma unroll
+                for (int t = 0; t < 8; ++t) pf[cc][t] = static_cast<__bf16>(s[8 * cc + t]);
+        }
     };
     // this wave's share of the tile traffic in V_j: publish tile j+lead, prefetch tile j+lead+1
     const int lead = grp == 0 ? 1 : 2;
@@ -826,6 +911,64 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     }
 }
 
+// ===========================================================================
+// e4m3 V^T for the FP8 P*V product: per 64-key tile and column d, the block
+// exponent e is the largest integer with amax * 2^e <= 448 (clipped to
+// [-127, 127]; 0 for an all-zero column), codes are e4m3(V * 2^e) rounded to
+// nearest even, stored transposed with the keys of each tile in f8_slot
+// order, and the byte 127 - e (the matrix core's exponent that undoes 2^e)
+// goes to vscale [BH, n_tiles, D].
+// ===========================================================================
+template <int D>
+__global__ __launch_bounds__(256) void quant_v_pow2_kernel(const uint8_t* __restrict__ v, uint8_t* __restrict__ v8,
+                                                           uint8_t* __restrict__ vscale, int N, int np, int n_tiles) {
+    constexpr int ROW = 2 * D + 16;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[kKeyTile * ROW];
+    __shared__ int sexp[D];
+    const int bh = blockIdx.x / n_tiles, t = blockIdx.x - bh * n_tiles;
+    const int n0 = kKeyTile * t;
+    const uint8_t* src = v + (static_cast<size_t>(bh) * N + n0) * D * 2;
+    for (int c = threadIdx.x; c < kKeyTile * D / 8; c += 256) {
+        const int key = c / (D / 8), col = c - key * (D / 8);
+        const u32x4 x = n0 + key < N ? ld16(src + (key * D + 8 * col) * 2) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(tile + key * ROW + 16 * col) = x;
+    }
+    __syncthreads();
+    auto val = [&](int key, int d) -> float {
+        return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(tile + key * ROW + 2 * d)) << 16);
+    };
+    for (int d = threadIdx.x; d < D; d += 256) {
+        float amax = 0.0f;
+        for (int key = 0; key < kKeyTile; ++key) amax = fmaxf(amax, fabsf(val(key, d)));
+        int e = 0;
+        if (amax > 0.0f) {
+            int x;
+            const float m = frexpf(amax, &x);              // amax = m * 2^x, m in [0.5, 1); 448 = 0.875 * 2^9
+            e = m <= 0.875f ? 9 - x : 8 - x;
+            e = e > 127 ? 127 : (e < -127 ? -127 : e);
+        }
+        sexp[d] = e;
+        vscale[(static_cast<size_t>(bh) * n_tiles + t) * D + d] = static_cast<uint8_t>(127 - e);
+    }
+    __syncthreads();
+    uint8_t* dst = v8 + static_cast<size_t>(bh) * D * np + n0;
+    for (int c = threadIdx.x; c < D * (kKeyTile / 16); c += 256) {
+        const int d = c / (kKeyTile / 16), part = c - d * (kKeyTile / 16);
+        const int e = sexp[d];
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int pos = 16 * part + i;
+            // inverse of f8_slot
+            const int key = (((pos >> 4) & 1) << 5) | (((pos >> 2) & 3) << 3) | (((pos >> 5) & 1) << 2) | (pos & 3);
+            const uint32_t code = e4m3_code(ldexpf(val(key, d), e));
+            w[i >> 2] |= code << (8 * (i & 3));
+        }
+        *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(d) * np + 16 * part) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+
 template <int D, bool CAUSAL, bool FP8>
 hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
     kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
@@ -833,6 +976,16 @@ hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8, kModeDense>), dim3(static_cast<int>(grid)),
                        dim3(PPCfg<D, CAUSAL, FP8>::NT), 0, st, kp);
+    return hipGetLastError();
+}
+template <int D, bool CAUSAL>
+hipError_t launch_fp8pv(KParams kp, int BH, hipStream_t st) {
+    using C = PPCfg<D, CAUSAL, true, true>;
+    kp.n_qtiles = (kp.N + C::BM - 1) / C::BM;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, true, kModeDense, true>), dim3(static_cast<int>(grid)), dim3(C::NT),
+                       0, st, kp);
     return hipGetLastError();
 }
 template <int D, bool CAUSAL>
@@ -901,6 +1054,8 @@ hipError_t dispatch_d(const FwdArgs& a, const KParams& kp, hipStream_t st) {
             return a.causal ? launch_bf<D, true, false>(kp, BH, st) : launch_bf<D, false, false>(kp, BH, st);
         case Kind::FP8:
             return a.causal ? launch_bf<D, true, true>(kp, BH, st) : launch_bf<D, false, true>(kp, BH, st);
+        case Kind::FP8PV:
+            return a.causal ? launch_fp8pv<D, true>(kp, BH, st) : launch_fp8pv<D, false>(kp, BH, st);
     }
     return hipErrorInvalidValue;
 }
@@ -931,6 +1086,9 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.bs_list = a.bs_list;
     kp.bs_count = a.bs_count;
     kp.bs_stride = a.bs_stride;
+    kp.vscale = a.v_scale;
+    if (a.kind == Kind::FP8PV && (a.v_scale == nullptr || a.o32 != nullptr || a.bs_list != nullptr))
+        return hipErrorInvalidValue;
     if (a.o32 != nullptr && (a.kind != Kind::BF16 || a.n_splits < 1 || a.tps < 1)) return hipErrorInvalidValue;
     if (a.bs_list != nullptr && (a.kind != Kind::BF16 || a.o32 != nullptr)) return hipErrorInvalidValue;
     switch (a.d) {
@@ -966,6 +1124,22 @@ hipError_t launch_bs_plan(const uint8_t* mask, long long mask_bh_stride, int BH,
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bs_plan_kernel, dim3(static_cast<int>(grid)), dim3(256), 0, stream, mask, mask_bh_stride, BH,
                        n_qtiles, nb, causal, list, count);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_v_pow2(const void* v, uint8_t* v8, uint8_t* vscale, int BH, int N, int d,
+                              hipStream_t stream) {
+    const int n_tiles = (N + kKeyTile - 1) / kKeyTile;
+    const int np = n_tiles * kKeyTile;
+    const long long grid = static_cast<long long>(BH) * n_tiles;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    const uint8_t* src = static_cast<const uint8_t*>(v);
+    switch (d) {
+        case 32: hipLaunchKernelGGL(quant_v_pow2_kernel<32>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, v8, vscale, N, np, n_tiles); break;
+        case 64: hipLaunchKernelGGL(quant_v_pow2_kernel<64>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, v8, vscale, N, np, n_tiles); break;
+        case 128: hipLaunchKernelGGL(quant_v_pow2_kernel<128>, dim3(static_cast<int>(grid)), dim3(256), 0, stream, src, v8, vscale, N, np, n_tiles); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -6,14 +6,15 @@
 
 namespace fa {
 
-enum class Kind { F32, BF16, FP8 };
+enum class Kind { F32, BF16, FP8, FP8PV };
 
 struct FwdArgs {
     Kind kind;
     const void* q;          // f32 / bf16 / e4m3 codes
     const void* k;
     const void* v;          // f32 or bf16
-    const void* vt;         // bf16/FP8 kernels: V transposed by launch_transpose_v, [BH, d, np]
+    const void* vt;         // bf16/FP8 kernels: V transposed by launch_transpose_v, [BH, d, np];
+                            // FP8PV: e4m3 V^T from launch_quant_v_pow2, [BH, d, np] bytes
     void* o;                // f32 or bf16
     float* lse;             // may be null
     const float* q_scale;   // FP8 only: [BH, ceil(N/64)]
@@ -37,6 +38,8 @@ struct FwdArgs {
     const uint32_t* bs_list = nullptr;
     const int* bs_count = nullptr;
     int bs_stride = 0;
+    // FP8PV: block-exponent bytes of the e4m3 V^T, [BH, ceil(N/64), d]
+    const uint8_t* v_scale = nullptr;
 };
 
 // Query rows per workgroup of the bf16/FP8 attention kernel (four 64-row blocks).
@@ -91,6 +94,14 @@ struct BwdArgs {
 
 // Enqueue the backward kernels (row statistics, dK/dV, dQ) on `stream`.
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+
+// Enqueue the power-of-two e4m3 quantisation of a bf16 V [BH, N, d] for the
+// FP8 P*V kernel: v8 [BH, d, np] bytes (np = N rounded up to 64, keys of each
+// tile in the order the kernel's P operand uses), vscale [BH, ceil(N/64), d]
+// bytes 127 - e with e the largest integer (clipped to +-127) for which the
+// tile column's amax * 2^e <= 448.
+hipError_t launch_quant_v_pow2(const void* v, uint8_t* v8, uint8_t* vscale, int BH, int N, int d,
+                              hipStream_t stream);
 
 // Enqueue the per-64-row-tile e4m3fn quantisation of a bf16 [BH, N, d] tensor.
 hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale,

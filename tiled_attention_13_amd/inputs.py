@@ -82,9 +82,12 @@ class Workload:
             io = 4 * elems * 4
         elif self.dtype == "bf16":
             io = 4 * elems * 2
-        else:  # fp8 Q/K codes, bf16 V and O, one fp32 scale per 64-row tile of Q and of K
+        elif self.dtype == "fp8":  # fp8 Q/K codes, bf16 V and O, one fp32 scale per 64-row tile of Q and of K
             tiles = self.B * self.H * ((self.N + 63) // 64)
             io = 2 * elems * 1 + 2 * elems * 2 + 2 * tiles * 4
+        else:  # fp8pv: fp8 Q/K/V codes, bf16 O, Q/K tile scales and one exponent byte per (tile, column) of V
+            tiles = self.B * self.H * ((self.N + 63) // 64)
+            io = 3 * elems * 1 + elems * 2 + 2 * tiles * 4 + tiles * self.d
         return io + self.B * self.H * self.N * 4
 
 
@@ -104,6 +107,9 @@ WORKLOADS: dict[str, Workload] = {
                         note="bf16 causal long sequence, 1% of K rows x8"),
     "c5_fp8": Workload("c5_fp8", 1, 16, 32768, 128, "fp8", True, 5,
                        note="fp8 e4m3 Q/K with per-64-row scales, bf16 V, causal"),
+    # the same tensors with P*V on e4m3 as well (the next row after the five)
+    "c5_fp8pv": Workload("c5_fp8pv", 1, 16, 32768, 128, "fp8pv", True, 5,
+                         note="fp8 e4m3 Q/K (per-64-row scales) and V, P (power-of-two block scales), causal"),
 }
 
 
@@ -130,7 +136,7 @@ def make_inputs(w: Workload, seed: int | None = None, shape: tuple | None = None
             for h in range(H):
                 rows = rng.choice(N, n_spike, replace=False)
                 k[b, h, rows, :] *= np.float32(w.spike_gain)
-    if w.dtype in ("bf16", "fp8"):
+    if w.dtype in ("bf16", "fp8", "fp8pv"):
         q, k, v = round_to_bf16(q), round_to_bf16(k), round_to_bf16(v)
     return q, k, v
 
