@@ -19,6 +19,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Word 3 of a raw buffer resource on gfx9-class GPUs (32-bit data format; no
+// swizzle, no stride): loads through it are range-checked against the
+// resource's byte count and return 0 past it.
+constexpr int kBufferFlags = 0x00020000;
+
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

@@ -305,40 +305,38 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     u32x4 vst[C::V_PER_T];
     u32x4 sst = {0, 0, 0, 0};                    // FP8 P*V: V block exponents of the tile
     const int n_all_tiles = (N + BN - 1) / BN;
+    // Tile copies go through buffer loads: the tile's base and the number of
+    // valid bytes live in scalar registers, each thread's offset within the tile
+    // is fixed, and rows past the end of the sequence read as zero (the hardware
+    // range check), so full and partial tiles share one path.
     auto load_tile = [&](int t) {
         const int n0 = tile_of(t) * BN;
-        const uint8_t* kt = kg + static_cast<size_t>(n0) * D * ES;
-        const uint8_t* vt = vtg + static_cast<size_t>(n0) * C::VES;
+        // (byte counts fit 32 bits: B*H*N*d < 2^31 elements of at most 2 bytes)
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(kg + static_cast<size_t>(n0) * D * ES), 0,
+            static_cast<int>(static_cast<uint32_t>(min(N - n0, BN) * D * ES)), kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(vtg + static_cast<size_t>(n0) * C::VES), 0,
+            static_cast<int>((static_cast<uint32_t>(D) * p.np - n0) * C::VES), kBufferFlags);
         if constexpr (PV8) {
             if (tid < C::SBYTES / 16)
                 sst = ld16(p.vscale + (static_cast<size_t>(bh) * n_all_tiles + tile_of(t)) * D + 16 * tid);
         }
-        if (n0 + BN <= N) {                        // full tile: no per-row guards
 #pragma unroll
-            for (int i = 0; i < C::K_PER_T; ++i) {
-                const int c = i * NT + tid;
-                if (c < C::K_CHUNKS) {
-                    const int row = c / C::K_CPR, col = c - row * C::K_CPR;
-                    kst[i] = ld16(kt + row * D * ES + 16 * col);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::K_PER_T; ++i) {
-                const int c = i * NT + tid;
-                if (c < C::K_CHUNKS) {
-                    const int row = c / C::K_CPR, col = c - row * C::K_CPR;
-                    kst[i] = n0 + row < N ? ld16(kt + row * D * ES + 16 * col) : u32x4{0, 0, 0, 0};
-                }
+        for (int i = 0; i < C::K_PER_T; ++i) {
+            const int c = i * NT + tid;
+            if (c < C::K_CHUNKS) {
+                const int row = c / C::K_CPR, col = c - row * C::K_CPR;
+                kst[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, row * D * ES + 16 * col, 0, 0);
             }
         }
-        // V^T rows are padded with zeros up to np, so no guard is needed
 #pragma unroll
         for (int i = 0; i < C::V_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
                 const int d = c / C::V_CPR, col = c - d * C::V_CPR;
-                vst[i] = ld16(vt + static_cast<size_t>(d) * p.np * C::VES + 16 * col);
+                vst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    vr, static_cast<int>(static_cast<uint32_t>(d) * p.np * C::VES + 16 * col), 0, 0);
             }
         }
     };
