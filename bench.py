@@ -20,8 +20,8 @@ mask leave visible.
 It also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
 seeded upstream gradient) timed the same way on the same bf16 workload,
 with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
-matrix-core FLOPs the kernels actually execute (3.5 x: the dQ kernel
-recomputes S and dP).
+matrix-core FLOPs the kernels actually execute (4 x: the dV, dK and dQ
+kernels each recompute S, and dK and dQ both compute dP).
 
 ``--calib-copy-mib`` runs, after the timed loop, a plain device copy of M MiB
 so that a counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) sees a kernel
@@ -208,13 +208,13 @@ def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
     per_call = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
     ms = float(per_call.mean())
     conv = 2.5 * w.flops()
-    executed = 3.5 * w.flops()
+    executed = 4.0 * w.flops()     # S three times (dV, dK, dQ kernels), dP twice, dV, dK, dQ once
     return {"ms_per_call": round(ms, 4), "median_ms": round(float(np.median(per_call)), 4),
             "tflops": round(conv / (ms * 1e-3) / 1e12, 2),
             "flop_convention": "2.5 x forward FLOPs (dV, dP, dQ, dK plus the recomputed S)",
             "mfma_tflops_executed": round(executed / (ms * 1e-3) / 1e12, 2),
             "pct_mfma_peak": round(100.0 * executed / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2),
-            "kernels": "bwd_prep_kernel, 3 x transpose_v_kernel, bwd_dkdv_kernel, bwd_dq_kernel"}
+            "kernels": "bwd_prep_kernel, 3 x transpose_v_kernel, bwd_kv_kernel (dV), bwd_kv_kernel (dK), bwd_dq_kernel"}
 
 
 def _cpu_model() -> str:

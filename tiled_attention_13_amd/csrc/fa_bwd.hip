@@ -20,11 +20,13 @@
 //    S^T = K Q^T and dP^T = V dO^T give every lane the scores of one query,
 //    so lse and D are one value per lane, and dS^T lands in the B-operand
 //    layout of dQ^T += K^T dS^T.
-//  * bwd_dkdv_kernel: key-stationary.  A workgroup holds 128 keys (32 per
-//    wave, K and V in registers) and streams 64-query tiles of Q, dO, Q^T,
-//    dO^T, lse and D through LDS; S = Q K^T and dP = dO V^T give every lane
-//    the scores of one key, and P and dS land in the B-operand layout of
-//    dV^T += dO^T P and dK^T += Q^T dS.
+//  * bwd_kv_kernel<.., 0> (dV) and <.., 1> (dK): key-stationary.  A
+//    workgroup holds 256 keys (32 per wave, K and V in registers) and streams
+//    64-query tiles of Q, dO^T (dV) or Q, dO, Q^T, lse and D (dK) through
+//    LDS; S = Q K^T and dP = dO V^T give every lane the scores of one key,
+//    and P and dS land in the B-operand layout of dV^T += dO^T P and
+//    dK^T += Q^T dS.  Splitting the two keeps each under 256 VGPRs, two
+//    waves per SIMD, at the price of computing S twice.
 //
 // The transposed operands (K^T, Q^T, dO^T) come from the same pre-pass the
 // forward uses for V^T, with rows permuted within each 16-group so that a
@@ -276,35 +278,41 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
 }
 
 // ===========================================================================
-// dK, dV: 4 waves x 32 keys, 64-query tiles of Q, dO, Q^T, dO^T, lse and D
-// in a 2-stage LDS ring.  One wave per SIMD (the accumulators of dK and dV
-// and the K and V operands take most of the register file).
+// dV and dK as two key-stationary kernels of 8 waves x 32 keys (two waves per
+// SIMD, so one wave's softmax work overlaps the other's matrix-core work):
+//   WHICH = 0: S = Q K^T, P = exp2(S c - lse2), dV^T += dO^T P     (Q rows, dO^T, lse2 streamed)
+//   WHICH = 1: S, dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS     (Q rows, dO rows, Q^T, lse2, D)
+// S is recomputed by both (2 + 3 products instead of 4 in one kernel); each
+// keeps its accumulator, K (and V) in registers and streams 64-query tiles
+// through a 2-stage LDS ring.
 // ===========================================================================
-template <int D>
-struct DkvCfg {
-    static constexpr int NW = 4;
+template <int D, int WHICH>
+struct KvCfg {
+    static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int BK = 32 * NW;                   // keys per workgroup
     static constexpr int BQ = 64;                        // queries per tile
     static constexpr int RROW = 2 * D + 16;              // bytes per Q / dO row in LDS (padded)
-    static constexpr int TROW = 2 * BQ + 16;             // bytes per Q^T / dO^T row in LDS (padded)
+    static constexpr int TROW = 2 * BQ + 16;             // bytes per dO^T / Q^T row in LDS (padded)
     static constexpr int RBYTES = BQ * RROW;
     static constexpr int TBYTES = D * TROW;
-    static constexpr int VEC = BQ * 4;                   // lse2 or D of one tile, bytes
-    static constexpr int STAGE = 2 * RBYTES + 2 * TBYTES + 2 * VEC;
+    static constexpr int NR = WHICH == 0 ? 1 : 2;        // row-major tiles: Q (and dO)
+    static constexpr int VEC = BQ * 4;
+    static constexpr int NV = WHICH == 0 ? 1 : 2;        // row vectors: lse2 (and D)
+    static constexpr int STAGE = NR * RBYTES + TBYTES + NV * VEC;
     static constexpr int R_CPR = D / 8;
     static constexpr int R_CHUNKS = BQ * R_CPR;
     static constexpr int T_CPR = 2 * BQ / 16;
     static constexpr int T_CHUNKS = D * T_CPR;
-    static constexpr int V_CHUNKS = 2 * VEC / 16;        // lse2 then D
+    static constexpr int V_CHUNKS = NV * VEC / 16;
     static constexpr int R_PER_T = (R_CHUNKS + NT - 1) / NT;
     static constexpr int T_PER_T = (T_CHUNKS + NT - 1) / NT;
     static constexpr int QREGS = D / 16;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
-    using C = DkvCfg<D>;
+template <int D, bool CAUSAL, int WHICH>
+__global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
+    using C = KvCfg<D, WHICH>;
     constexpr int BK = C::BK, BQ = C::BQ, NT = C::NT;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
@@ -319,52 +327,55 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* qg = p.q + slice * 2;
     const uint8_t* gg = p.dout + slice * 2;
-    const uint8_t* qtg = p.qt + static_cast<size_t>(bh) * D * p.np * 2;
-    const uint8_t* gtg = p.dot + static_cast<size_t>(bh) * D * p.np * 2;
+    const uint8_t* tg = (WHICH == 0 ? p.dot : p.qt) + static_cast<size_t>(bh) * D * p.np * 2;
     const float* l2g = p.lse2 + static_cast<size_t>(bh) * N;
     const float* dsg = p.dsum + static_cast<size_t>(bh) * N;
 
-    // K and V rows of this lane's key: B operands of S = Q K^T and dP = dO V^T
-    u32x4 kf[C::QREGS], vf[C::QREGS];
+    // K (and V) rows of this lane's key: B operands of S = Q K^T (and dP = dO V^T)
+    u32x4 kf[C::QREGS], vf[WHICH == 1 ? C::QREGS : 1];
     {
         const bool ok = my_k < N;
         const size_t off = (slice + static_cast<size_t>(my_k) * D) * 2;
 #pragma unroll
         for (int i = 0; i < C::QREGS; ++i) {
             kf[i] = ok ? ld16(p.k + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
-            vf[i] = ok ? ld16(p.v + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+            if constexpr (WHICH == 1) vf[i] = ok ? ld16(p.v + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
         }
     }
 
     const int n_qt = (N + BQ - 1) / BQ;
     const int t0 = CAUSAL ? min(k0 / BQ, n_qt) : 0;
-    // first tile holding a query at or after this wave's first key
-    const int t_first = CAUSAL ? max(t0, kw0 / BQ) : 0;
+    const int t_first = CAUSAL ? max(t0, kw0 / BQ) : 0;  // first tile with a query at or after this wave's keys
 
-    // A tile is copied in two parts (part 0: Q rows, Q^T, lse2 and D; part 1:
-    // dO rows, dO^T), each loaded from global memory just before one 32-query
-    // block of the current tile is computed and written to LDS right after it,
-    // so only half a tile is ever staged in registers.
+    // Tile copy in two parts around the two 32-query blocks of the current
+    // tile (part 0: Q rows and the row vectors; part 1: the transposed tile and,
+    // for dK, the dO rows), through buffer loads whose range check zero-fills
+    // rows past the end of the sequence.
     u32x4 rst[C::R_PER_T], tst[C::T_PER_T], vecst;
     auto load_part = [&](int t, int part) {
         const int m0 = t * BQ;
-        const uint8_t* rg = part == 0 ? qg : gg;
-        const uint8_t* tg = part == 0 ? qtg : gtg;
+        const int valid = min(N - m0, BQ) * D * 2;
+        if (part == 0 || WHICH == 1) {
+            const uint8_t* rg = part == 0 ? qg : gg;
+            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(rg + static_cast<size_t>(m0) * D * 2), 0, valid, kBufferFlags);
 #pragma unroll
-        for (int i = 0; i < C::R_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < C::R_CHUNKS) {
-                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                const size_t off = (static_cast<size_t>(m0 + row) * D + 8 * col) * 2;
-                rst[i] = m0 + row < N ? ld16(rg + off) : u32x4{0, 0, 0, 0};
+            for (int i = 0; i < C::R_PER_T; ++i) {
+                const int c = i * NT + tid;
+                if (c < C::R_CHUNKS) {
+                    const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+                    rst[i] = __builtin_amdgcn_raw_buffer_load_b128(rr, row * D * 2 + 16 * col, 0, 0);
+                }
             }
         }
+        if (part == 1) {
 #pragma unroll
-        for (int i = 0; i < C::T_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < C::T_CHUNKS) {
-                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                tst[i] = ld16(tg + (static_cast<size_t>(d) * p.np + m0) * 2 + 16 * col);
+            for (int i = 0; i < C::T_PER_T; ++i) {
+                const int c = i * NT + tid;
+                if (c < C::T_CHUNKS) {
+                    const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+                    tst[i] = ld16(tg + (static_cast<size_t>(d) * p.np + m0) * 2 + 16 * col);
+                }
             }
         }
         if (part == 0 && tid < C::V_CHUNKS) {
@@ -378,46 +389,45 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
     };
     auto store_part = [&](int t, int part) {
         uint8_t* stage = smem + (t & 1) * C::STAGE;
-        uint8_t* rs = stage + part * C::RBYTES;
-        uint8_t* ts = stage + 2 * C::RBYTES + part * C::TBYTES;
+        if (part == 0 || WHICH == 1) {
+            uint8_t* rs = stage + part * C::RBYTES;
 #pragma unroll
-        for (int i = 0; i < C::R_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < C::R_CHUNKS) {
-                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                *reinterpret_cast<u32x4*>(rs + row * C::RROW + 16 * col) = rst[i];
+            for (int i = 0; i < C::R_PER_T; ++i) {
+                const int c = i * NT + tid;
+                if (c < C::R_CHUNKS) {
+                    const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+                    *reinterpret_cast<u32x4*>(rs + row * C::RROW + 16 * col) = rst[i];
+                }
             }
         }
+        if (part == 1) {
+            uint8_t* ts = stage + C::NR * C::RBYTES;
 #pragma unroll
-        for (int i = 0; i < C::T_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < C::T_CHUNKS) {
-                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
+            for (int i = 0; i < C::T_PER_T; ++i) {
+                const int c = i * NT + tid;
+                if (c < C::T_CHUNKS) {
+                    const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+                    *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
+                }
             }
         }
         if (part == 0 && tid < C::V_CHUNKS)
-            *reinterpret_cast<u32x4*>(stage + 2 * C::RBYTES + 2 * C::TBYTES + 16 * tid) = vecst;
+            *reinterpret_cast<u32x4*>(stage + C::NR * C::RBYTES + C::TBYTES + 16 * tid) = vecst;
     };
 
-    f32x16 dk[D / 32], dv[D / 32];
+    f32x16 acc[D / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
 
-    // one 32-query block qb of tile t: S and dP, then its share of dV and dK
+    // one 32-query block qb of tile t
     auto compute = [&](int t, int qb, bool masked) {
-        const uint8_t* qs = smem + (t & 1) * C::STAGE;
-        const uint8_t* gs = qs + C::RBYTES;
-        const uint8_t* qts = gs + C::RBYTES;
-        const uint8_t* gts = qts + C::TBYTES;
-        const float* l2s = reinterpret_cast<const float*>(gts + C::TBYTES);
+        const uint8_t* stage = smem + (t & 1) * C::STAGE;
+        const uint8_t* qs = stage;
+        const uint8_t* gs = stage + C::RBYTES;           // dO rows (dK only)
+        const uint8_t* ts = stage + C::NR * C::RBYTES;
+        const float* l2s = reinterpret_cast<const float*>(ts + C::TBYTES);
         const float* dss = l2s + BQ;
-        // causal: key my_k is masked for query row 32*qb + 8*(v/4) + 4*h + v%4 of the tile when
-        // rel > 8*(v/4) + v%4
-        const int rel = my_k - t * BQ - 32 * qb - 4 * h;
+        const int rel = my_k - t * BQ - 32 * qb - 4 * h; // masked when rel > 8*(v/4) + v%4
         f32x16 s = {}, dp = {};
         const uint8_t* qr = qs + (32 * qb + l32) * C::RROW + 16 * h;
         const uint8_t* gr = gs + (32 * qb + l32) * C::RROW + 16 * h;
@@ -425,47 +435,40 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
         for (int i = 0; i < C::QREGS; ++i) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(qr + 32 * i)),
                                                        __builtin_bit_cast(bf16x8, kf[i]), s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(gr + 32 * i)),
-                                                        __builtin_bit_cast(bf16x8, vf[i]), dp, 0, 0, 0);
+            if constexpr (WHICH == 1)
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(gr + 32 * i)),
+                                                            __builtin_bit_cast(bf16x8, vf[i]), dp, 0, 0, 0);
         }
-        float pv[16], dsv[16];
+        float x[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * qb + 8 * g + 4 * h);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
+            f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (WHICH == 1) d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int v = 4 * g + e;
                 float pr = fast_exp2(fmaf(s[v], p.c_log2, -l4[e]));
                 if (masked && CAUSAL && rel > 8 * g + e) pr = 0.0f;
-                pv[v] = pr;
-                dsv[v] = pr * (dp[v] - d4[e]);
+                x[v] = WHICH == 0 ? pr : pr * (dp[v] - d4[e]);
             }
         }
-        bf16x8 pf[2], dsf[2];
+        bf16x8 xf[2];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pf[cc][e] = static_cast<__bf16>(pv[8 * cc + e]);
-                dsf[cc][e] = static_cast<__bf16>(dsv[8 * cc + e]);
-            }
-        const uint8_t* gtr = gts + l32 * C::TROW + 16 * h;
-        const uint8_t* qtr = qts + l32 * C::TROW + 16 * h;
+            for (int e = 0; e < 8; ++e) xf[cc][e] = static_cast<__bf16>(x[8 * cc + e]);
+        const uint8_t* tr = ts + l32 * C::TROW + 16 * h;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int col = 32 * (2 * qb + cc);
-                dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, ld16(gtr + 32 * db * C::TROW + col)), pf[cc], dv[db], 0, 0, 0);
-                dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, ld16(qtr + 32 * db * C::TROW + col)), dsf[cc], dk[db], 0, 0, 0);
-            }
+            for (int cc = 0; cc < 2; ++cc)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * (2 * qb + cc))), xf[cc], acc[db], 0,
+                    0, 0);
     };
     auto compute_block = [&](int t, int qb) {
         if (t < t_first) return;
-        // a causal mask is needed while the tile starts before this wave's last key
         compute(t, qb, CAUSAL && t * BQ < kw0 + 31);
     };
 
@@ -490,19 +493,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BParams p) {
     }
 
     if (my_k < N) {
-        const size_t off = (slice + static_cast<size_t>(my_k) * D) * 2;
+        uint8_t* out = (WHICH == 0 ? p.dv : p.dk) + (slice + static_cast<size_t>(my_k) * D) * 2;
+        const float mul = WHICH == 0 ? 1.0f : p.scale;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                bf16x4 ok_, ov;
+                bf16x4 ov;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    ok_[e] = static_cast<__bf16>(dk[db][4 * g + e] * p.scale);
-                    ov[e] = static_cast<__bf16>(dv[db][4 * g + e]);
-                }
-                *reinterpret_cast<bf16x4*>(p.dk + off + 2 * (32 * db + 8 * g + 4 * h)) = ok_;
-                *reinterpret_cast<bf16x4*>(p.dv + off + 2 * (32 * db + 8 * g + 4 * h)) = ov;
+                for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(acc[db][4 * g + e] * mul);
+                *reinterpret_cast<bf16x4*>(out + 2 * (32 * db + 8 * g + 4 * h)) = ov;
             }
     }
 }
@@ -521,10 +521,12 @@ hipError_t launch_bwd_d(BParams bp, const void* o, const float* lse, float* lse2
     a.n_tiles = (bp.N + DqCfg<D>::BM - 1) / DqCfg<D>::BM;
     const long long g1 = static_cast<long long>(a.n_tiles) * bp.BH;
     BParams b = bp;
-    b.n_tiles = (bp.N + DkvCfg<D>::BK - 1) / DkvCfg<D>::BK;
+    b.n_tiles = (bp.N + KvCfg<D, 0>::BK - 1) / KvCfg<D, 0>::BK;
     const long long g2 = static_cast<long long>(b.n_tiles) * bp.BH;
     if (g1 > 0x7FFFFFFFLL || g2 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(static_cast<int>(g2)), dim3(DkvCfg<D>::NT), 0, st, b);
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 0>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 0>::NT), 0, st, b);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 1>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 1>::NT), 0, st, b);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<int>(g1)), dim3(DqCfg<D>::NT), 0, st, a);
     return hipGetLastError();
