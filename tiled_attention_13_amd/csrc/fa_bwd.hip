@@ -157,47 +157,56 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
     const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
     const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
 
-    u32x4 kst[C::R_PER_T], vst[C::R_PER_T], tst[C::T_PER_T];
-    auto load_tile = [&](int t) {
-        const int n0 = t * BN;
+    // A tile is copied in two halves of 32 keys (K and V rows, and the matching
+    // 32 key slots of every K^T row), each loaded just before one 32-key block of
+    // the current tile is computed and written to LDS right after it.  Buffer
+    // loads: rows past the end of the sequence read as zero.
+    constexpr int HR = C::R_CHUNKS / 2, HT = C::T_CHUNKS / 2;      // chunks per half
+    constexpr int HR_PER_T = (HR + NT - 1) / NT, HT_PER_T = (HT + NT - 1) / NT;
+    u32x4 kst[HR_PER_T], vst[HR_PER_T], tst[HT_PER_T];
+    auto load_half = [&](int t, int half) {
+        const int n0 = t * BN + 32 * half;
+        const int valid = max(0, min(N - n0, 32)) * D * 2;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(kg + static_cast<size_t>(min(n0, N)) * D * 2), 0, valid, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(vg + static_cast<size_t>(min(n0, N)) * D * 2), 0, valid, kBufferFlags);
 #pragma unroll
-        for (int i = 0; i < C::R_PER_T; ++i) {
+        for (int i = 0; i < HR_PER_T; ++i) {
             const int c = i * NT + tid;
-            if (c < C::R_CHUNKS) {
+            if (c < HR) {
                 const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                const bool ok = n0 + row < N;
-                const size_t off = (static_cast<size_t>(n0 + row) * D + 8 * col) * 2;
-                kst[i] = ok ? ld16(kg + off) : u32x4{0, 0, 0, 0};
-                vst[i] = ok ? ld16(vg + off) : u32x4{0, 0, 0, 0};
+                kst[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, row * D * 2 + 16 * col, 0, 0);
+                vst[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, row * D * 2 + 16 * col, 0, 0);
             }
         }
 #pragma unroll
-        for (int i = 0; i < C::T_PER_T; ++i) {
+        for (int i = 0; i < HT_PER_T; ++i) {
             const int c = i * NT + tid;
-            if (c < C::T_CHUNKS) {
-                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                tst[i] = ld16(ktg + (static_cast<size_t>(d) * p.np + n0) * 2 + 16 * col);
+            if (c < HT) {
+                const int d = c / (C::T_CPR / 2), col = c - d * (C::T_CPR / 2) + half * (C::T_CPR / 2);
+                tst[i] = ld16(ktg + (static_cast<size_t>(d) * p.np + t * BN) * 2 + 16 * col);
             }
         }
     };
-    auto store_tile = [&](int t) {
+    auto store_half = [&](int t, int half) {
         uint8_t* ks = smem + (t & 1) * C::STAGE;
         uint8_t* vs = ks + C::KBYTES;
         uint8_t* ts = vs + C::KBYTES;
 #pragma unroll
-        for (int i = 0; i < C::R_PER_T; ++i) {
+        for (int i = 0; i < HR_PER_T; ++i) {
             const int c = i * NT + tid;
-            if (c < C::R_CHUNKS) {
-                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
+            if (c < HR) {
+                const int row = c / C::R_CPR + 32 * half, col = c - (c / C::R_CPR) * C::R_CPR;
                 *reinterpret_cast<u32x4*>(ks + row * C::KROW + 16 * col) = kst[i];
                 *reinterpret_cast<u32x4*>(vs + row * C::KROW + 16 * col) = vst[i];
             }
         }
 #pragma unroll
-        for (int i = 0; i < C::T_PER_T; ++i) {
+        for (int i = 0; i < HT_PER_T; ++i) {
             const int c = i * NT + tid;
-            if (c < C::T_CHUNKS) {
-                const int d = c / C::T_CPR, col = c - d * C::T_CPR;
+            if (c < HT) {
+                const int d = c / (C::T_CPR / 2), col = c - d * (C::T_CPR / 2) + half * (C::T_CPR / 2);
                 *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
             }
         }
@@ -207,59 +216,68 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
-    auto compute = [&](int j, bool masked) {
+    // one 32-key block kb of tile j: S^T, dP^T, dS^T, then its share of dQ^T
+    auto compute = [&](int j, int kb, bool masked) {
         const uint8_t* ks = smem + (j & 1) * C::STAGE;
         const uint8_t* vs = ks + C::KBYTES;
         const uint8_t* ts = vs + C::KBYTES;
         const int n0 = j * BN;
-        float ds[BN / 2];
+        f32x16 s = {}, dp = {};
+        const uint8_t* kr = ks + (32 * kb + l32) * C::KROW + 16 * h;
+        const uint8_t* vr = vs + (32 * kb + l32) * C::KROW + 16 * h;
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            f32x16 s = {}, dp = {};
-            const uint8_t* kr = ks + (32 * kb + l32) * C::KROW + 16 * h;
-            const uint8_t* vr = vs + (32 * kb + l32) * C::KROW + 16 * h;
-#pragma unroll
-            for (int i = 0; i < C::QREGS; ++i) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(kr + 32 * i)),
-                                                           __builtin_bit_cast(bf16x8, qf[i]), s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(vr + 32 * i)),
-                                                            __builtin_bit_cast(bf16x8, gf[i]), dp, 0, 0, 0);
-            }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float pr = fast_exp2(fmaf(s[v], p.c_log2, -lse2_q));
-                if (masked) {
-                    const int key = n0 + 32 * kb + acc_row(v, h);
-                    if (key >= N || (CAUSAL && key > my_q)) pr = 0.0f;
-                }
-                ds[16 * kb + v] = pr * (dp[v] - d_q);
-            }
+        for (int i = 0; i < C::QREGS; ++i) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(kr + 32 * i)),
+                                                       __builtin_bit_cast(bf16x8, qf[i]), s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ld16(vr + 32 * i)),
+                                                        __builtin_bit_cast(bf16x8, gf[i]), dp, 0, 0, 0);
         }
-        bf16x8 dsf[BN / 16];
+        float ds[16];
 #pragma unroll
-        for (int cc = 0; cc < BN / 16; ++cc)
+        for (int v = 0; v < 16; ++v) {
+            float pr = fast_exp2(fmaf(s[v], p.c_log2, -lse2_q));
+            if (masked) {
+                const int key = n0 + 32 * kb + acc_row(v, h);
+                if (key >= N || (CAUSAL && key > my_q)) pr = 0.0f;
+            }
+            ds[v] = pr * (dp[v] - d_q);
+        }
+        bf16x8 dsf[2];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
             for (int t = 0; t < 8; ++t) dsf[cc][t] = static_cast<__bf16>(ds[8 * cc + t]);
         const uint8_t* tr = ts + l32 * C::TROW + 16 * h;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int cc = 0; cc < BN / 16; ++cc)
+            for (int cc = 0; cc < 2; ++cc)
                 dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * cc)), dsf[cc], dq[db], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * (2 * kb + cc))), dsf[cc], dq[db], 0,
+                    0, 0);
+    };
+    auto compute_block = [&](int j, int kb) {
+        if (j > j_last) return;
+        // only the last tile of this wave can cross the diagonal or the sequence end
+        const int n0 = j * BN;
+        compute(j, kb, j == j_last && ((CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N));
     };
 
-    load_tile(0);
-    store_tile(0);
+    load_half(0, 0);
+    store_half(0, 0);
+    load_half(0, 1);
+    store_half(0, 1);
     __syncthreads();
     for (int j = 0; j < n_kt; ++j) {
-        if (j + 1 < n_kt) load_tile(j + 1);
-        if (j <= j_last) {
-            // only the last tile of this wave can cross the diagonal or the sequence end
-            const int n0 = j * BN;
-            compute(j, j == j_last && ((CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N));
+        const bool more = j + 1 < n_kt;
+        if (more) load_half(j + 1, 0);
+        compute_block(j, 0);
+        if (more) {
+            store_half(j + 1, 0);
+            load_half(j + 1, 1);
         }
-        if (j + 1 < n_kt) store_tile(j + 1);
+        compute_block(j, 1);
+        if (more) store_half(j + 1, 1);
         __syncthreads();
     }
 
