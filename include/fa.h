@@ -31,7 +31,7 @@
  *     sequence, head dim) in device memory.  Base pointers of q, k, v, o,
  *     q8, k8 must be 16-byte aligned; lse and scale pointers 4-byte aligned.
  *   - Supported head dims: d in {32, 64, 128}.  Any N >= 1 (tails are
- *     masked); B, H >= 1; B*H*N*d < 2^31.
+ *     masked); B, H >= 1; B*H*ceil(N/64)*64*d < 2^31.
  *   - Causal masking keeps key j for query i iff j <= i (square attention,
  *     Nq = Nk = N).
  *   - lse is float32 [B, H, N] and may be NULL (then it is not written).

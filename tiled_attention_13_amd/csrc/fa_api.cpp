@@ -1,4 +1,6 @@
-// C ABI of the attention forward library (declared in include/fa.h).
+// C ABI of the attention library (declared in include/fa.h): forward in four
+// element types, partial / merged / split-KV and block-sparse forwards, FP8
+// pre-passes, and the backward.
 //
 // Every argument is checked before the first HIP call, so argument errors come
 // back synchronously and can be exercised on a machine without a GPU.  After
@@ -28,8 +30,10 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_INVALID_SHAPE;
     if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
     // element offsets inside a launch are formed in 32-bit arithmetic per (b, h)
-    // slice and 64-bit across slices; keep the whole tensor below 2^31 elements
-    const long double total = static_cast<long double>(B) * H * N * d;
+    // slice and 64-bit across slices; keep the whole tensor, with N rounded up
+    // to the 64-key tile (the transposed workspaces), below 2^31 elements
+    const long double np = static_cast<long double>((N + 63) / 64 * 64);
+    const long double total = static_cast<long double>(B) * H * np * d;
     if (total >= 2147483648.0L) return FA_ERR_INVALID_SHAPE;
     return FA_OK;
 }
@@ -74,7 +78,7 @@ const char* fa_status_string(fa_status s) {
     switch (s) {
         case FA_OK: return "ok";
         case FA_ERR_NULL_POINTER: return "a required pointer is NULL";
-        case FA_ERR_INVALID_SHAPE: return "B, H, N must be >= 1 and B*H*N*d < 2^31";
+        case FA_ERR_INVALID_SHAPE: return "B, H, N must be >= 1 and B*H*ceil(N/64)*64*d < 2^31";
         case FA_ERR_UNSUPPORTED_HEAD_DIM: return "head dim must be 32, 64 or 128";
         case FA_ERR_INVALID_SCALE: return "softmax_scale must be finite and > 0";
         case FA_ERR_INVALID_DTYPE: return "unknown or unsupported dtype";
