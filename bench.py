@@ -7,7 +7,8 @@ halved for causal), ms per call, the roofline entry of the attention kernel
 and the float64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4_bf16]
-                    [--no-cpu-baseline] [--no-bwd] [--headline-only] [--calib-copy-mib M]
+                    [--no-cpu-baseline] [--no-bwd] [--no-configs] [--headline-only]
+                    [--calib-copy-mib M]
 
 The line also carries a ``splitkv`` object: ``fa_fwd`` against
 ``fa_fwd_splitkv`` (keys split into ranges run as separate workgroups, then
@@ -17,6 +18,11 @@ A ``blocksparse`` object times ``fa_fwd_blocksparse`` on the same workload
 with a sliding-window (16 blocks) plus global (2 blocks) table of 64x64
 blocks, TFLOP/s counted over the (query, key) pairs the table and the causal
 mask leave visible.
+A ``configs`` object times every other forward workload (fp32 128 x 64,
+the two d=32 shapes, bf16 4x32x4096x128 causal): median / p10 / p90 ms warm
+(back to back) and, for working sets under the 256 MB MALL, cold (a 512 MiB
+write before each call, outside the events) with HBM GB/s of the compulsory
+bytes; the d=32 shapes also carry a VALU estimate, their binding roof.
 It also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
 seeded upstream gradient) timed the same way on the same bf16 workload,
 with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
@@ -169,6 +175,80 @@ def bench_blocksparse(w, tq, tk, tv, steps: int):
             "blocks_total": total, "ms_per_call": round(ms, 4), "tflops_visible": round(flops / ms / 1e9, 2)}
 
 
+def _stats(ms: np.ndarray) -> dict:
+    return {"median": round(float(np.median(ms)), 5), "p10": round(float(np.percentile(ms, 10)), 5),
+            "p90": round(float(np.percentile(ms, 90)), 5)}
+
+
+def _time_cold(fn, steps: int, flush) -> np.ndarray:
+    """Per-call times with the caches flushed before every call (outside the events)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        flush(i)
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+
+
+# VALU estimate for the small-d shapes: per score about four full-rate VALU
+# instructions (scale-and-subtract FMA, running sum, half a max3, half a
+# bf16 pack) at 4 cycles per wave64 instruction, plus one v_exp_f32 at about
+# 12 cycles, over 256 CUs x 4 SIMDs at 2.4 GHz.
+VALU_CYCLES_PER_SCORE = (4 * 4 + 12) / 64.0
+N_SIMD = 256 * 4
+CLOCK_HZ = 2.4e9
+
+
+def bench_configs(flush_mib: int = 512):
+    """Every other forward workload once: warm (back to back) and, where the
+    working set fits the 256 MB MALL, cold (a 512 MiB write before each call).
+    HBM GB/s are compulsory bytes over the cold median."""
+    import torch
+    from tiled_attention_13_amd import fwd
+    from tiled_attention_13_amd.inputs import WORKLOADS, make_inputs
+    flush_buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
+    flush = lambda i: flush_buf.fill_(i & 0xFF)
+    out = {}
+    for name, steps in (("c1_f32", 200), ("c2_bf16", 200), ("c2_bf16_causal", 200), ("c3_bf16", 20)):
+        w = WORKLOADS[name]
+        tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        q, k, v = (torch.from_numpy(a).to("cuda").to(tdt) for a in make_inputs(w))
+        o = torch.empty_like(q)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+        call = lambda: fwd(q, k, v, causal=w.causal, dtype=w.dtype, out=o, lse=lse)
+        warm = _time_calls(call, steps, warmup=5)
+        med = float(np.median(warm))
+        r = {"shape": list(w.shape), "dtype": w.dtype, "causal": w.causal, "warm_ms": _stats(warm),
+             "tflops": round(w.flops() / med / 1e9, 3),
+             "pct_mfma_peak": round(100.0 * w.flops() / med / 1e9 / PEAK_TFLOPS[w.dtype], 2),
+             "compulsory_bytes": w.compulsory_bytes()}
+        if w.compulsory_bytes() < (256 << 20):
+            cold = _time_cold(call, min(steps, 50), flush)
+            cmed = float(np.median(cold))
+            r["cold_ms"] = _stats(cold)
+            r["hbm_gbps_cold"] = round(w.compulsory_bytes() / cmed / 1e6, 1)
+            r["pct_hbm_peak_cold"] = round(100.0 * w.compulsory_bytes() / cmed / 1e6 / PEAK_HBM_GBPS, 2)
+        if w.d <= 64 and w.dtype == "bf16":
+            scores = w.B * w.H * float(w.N) ** 2 * (0.5 if w.causal else 1.0)
+            r["valu_estimate_ms"] = round(scores * VALU_CYCLES_PER_SCORE / N_SIMD / CLOCK_HZ * 1e3, 4)
+            r["bound"] = "valu"
+        elif w.dtype == "f32":
+            r["bound"] = "launch latency"
+        else:
+            r["bound"] = "mfma"
+        out[name] = r
+        del q, k, v, o, lse
+    del flush_buf
+    return out
+
+
 def bench_fp8(steps: int):
     """The FP8 workload (1x16x32768x128 causal) with Q/K on e4m3 (bf16 P*V) and with P*V on e4m3 too."""
     import torch
@@ -183,7 +263,22 @@ def bench_fp8(steps: int):
         ms = float(_time_calls(lambda: fwd(q, k, v, causal=w.causal, dtype=dt, out=o, lse=lse), steps).mean())
         res[dt] = {"ms_per_call": round(ms, 4), "tflops": round(w.flops() / ms / 1e9, 2),
                    "pct_fp8_peak": round(100.0 * w.flops() / ms / 1e9 / PEAK_TFLOPS["fp8"], 2)}
-    res["note"] = "fp8: Q.K^T on e4m3, P.V on bf16; fp8pv: both on e4m3; quantisation pre-passes included"
+    # the attention kernel alone on pre-quantised Q/K (the pre-pass timed on its own)
+    from tiled_attention_13_amd import fwd_fp8, quant_fp8
+    pre = _time_calls(lambda: (quant_fp8(q), quant_fp8(k)), steps)
+    q8, qs = quant_fp8(q)
+    k8, ks = quant_fp8(k)
+    alone = _time_calls(lambda: fwd_fp8(q8, qs, k8, ks, v, causal=w.causal, out=o, lse=lse), steps)
+    ms = float(alone.mean())
+    # mixed ceiling: Q.K^T (half the FLOPs) at the fp8 peak, P.V at the bf16 peak
+    mixed = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
+    res["fp8"]["prepass_ms"] = round(float(pre.mean()), 4)
+    res["fp8"]["kernel_only"] = {"ms_per_call": round(ms, 4), "tflops": round(w.flops() / ms / 1e9, 2),
+                                 "pct_fp8_peak": round(100.0 * w.flops() / ms / 1e9 / PEAK_TFLOPS["fp8"], 2),
+                                 "pct_mixed_ceiling": round(100.0 * w.flops() / ms / 1e9 / mixed, 2),
+                                 "mixed_ceiling_tflops": round(mixed, 1)}
+    res["note"] = ("fp8: Q.K^T on e4m3, P.V on bf16; fp8pv: both on e4m3; ms_per_call includes the "
+                   "quantisation pre-passes, kernel_only is fa_fwd_fp8 on pre-quantised Q/K")
     return res
 
 
@@ -238,6 +333,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0)
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload object (fp32, the two small-d shapes, the B=4 N=4096 shape)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline fa_fwd (no split-KV, block-sparse or backward objects)")
     args = ap.parse_args()
@@ -333,6 +430,8 @@ def main():
         result["blocksparse"] = bench_blocksparse(w, dq, dk, dv, args.steps)
     if extras:
         result["fp8"] = bench_fp8(args.steps)
+    if extras and not args.no_configs:
+        result["configs"] = bench_configs()
     if extras and not args.no_bwd:
         result["backward"] = bench_backward(w, dq, dk, dv, out, lse, args.steps, args.warmup)
     if not args.no_cpu_baseline:

@@ -189,16 +189,23 @@ struct PPCfg {
     static constexpr int K_CPR = D * ES / 16;    // 16-byte chunks per K row
     static constexpr int K_CHUNKS = BN * K_CPR;
     static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-    static constexpr int V_CPR = VES * BN / 16;  // 16-byte chunks per V^T row of a tile
-    static constexpr int V_CHUNKS = D * V_CPR;   // 16-byte chunks of a V^T tile (D rows x BN keys)
+    // small heads read V [N, d] rows and transpose each tile into LDS; the
+    // others copy rows of the V^T workspace
+    static constexpr bool VNAT = !PV8 && D < kVtMinD;
+    static constexpr int V_CPR = VNAT ? D * 2 / 16 : VES * BN / 16;   // 16-byte chunks per V (V^T) row
+    static constexpr int V_CHUNKS = VNAT ? BN * V_CPR : D * V_CPR;    // 16-byte chunks of a V tile
     static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
     static constexpr bool F8W = FP8 && (D % 64 == 0);
     static constexpr bool F8N = FP8 && !F8W;
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
 
+// Dense kernels for heads below 128 ask for 128 VGPRs (four waves per SIMD: two
+// workgroups per CU); the partial-result and block-sparse modes keep the wider
+// budget, which they need.
 template <int D, bool CAUSAL, bool FP8, int MODE, bool PV8 = false>
-__global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((D < 128 && MODE == kModeDense) ? 4 : 2)))
+void fwd_pp_kernel(KParams p) {
     using C = PPCfg<D, CAUSAL, FP8, PV8>;
     constexpr bool PARTIAL = MODE == kModePartial, SPARSE = MODE == kModeSparse;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, ES = C::ES;
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
     const uint8_t* qg = p.q + slice * ES;
     const uint8_t* kg = p.k + slice * ES;
     // V^T rows of this (b, h): D rows of np keys
-    const uint8_t* vtg = p.vt + static_cast<size_t>(bh) * D * p.np * C::VES;
+    const uint8_t* vtg = C::VNAT ? p.v + slice * 2 : p.vt + static_cast<size_t>(bh) * D * p.np * C::VES;
 
     // ---- Q fragments (B operand of S^T = K Q^T)
     u32x4 qf[C::F8W ? 2 * C::QREGS : C::QREGS];
@@ -315,9 +322,13 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(kg + static_cast<size_t>(n0) * D * ES), 0,
             static_cast<int>(static_cast<uint32_t>(min(N - n0, BN) * D * ES)), kBufferFlags);
-        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(vtg + static_cast<size_t>(n0) * C::VES), 0,
-            static_cast<int>((static_cast<uint32_t>(D) * p.np - n0) * C::VES), kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = C::VNAT
+            ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vtg + static_cast<size_t>(n0) * D * 2), 0,
+                                                static_cast<int>(static_cast<uint32_t>(min(N - n0, BN) * D * 2)),
+                                                kBufferFlags)
+            : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vtg + static_cast<size_t>(n0) * C::VES), 0,
+                                                static_cast<int>((static_cast<uint32_t>(D) * p.np - n0) * C::VES),
+                                                kBufferFlags);
         if constexpr (PV8) {
             if (tid < C::SBYTES / 16)
                 sst = ld16(p.vscale + (static_cast<size_t>(bh) * n_all_tiles + tile_of(t)) * D + 16 * tid);
@@ -334,9 +345,10 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
         for (int i = 0; i < C::V_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
-                const int d = c / C::V_CPR, col = c - d * C::V_CPR;
+                const int d = c / C::V_CPR, col = c - d * C::V_CPR;   // (VNAT: d is the key)
                 vst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    vr, static_cast<int>(static_cast<uint32_t>(d) * p.np * C::VES + 16 * col), 0, 0);
+                    vr, C::VNAT ? d * D * 2 + 16 * col
+                                : static_cast<int>(static_cast<uint32_t>(d) * p.np * C::VES + 16 * col), 0, 0);
             }
         }
     };
@@ -356,7 +368,19 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(KParams p) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
                 const int d = c / C::V_CPR, col = c - d * C::V_CPR;
-                *reinterpret_cast<u32x4*>(vs + d * C::VROW + 16 * col) = vst[i];
+                if constexpr (C::VNAT) {
+                    // key d, dims 8 col .. 8 col + 7: one bf16 into each V^T row, at the
+                    // key's slot (vt_slot is its own inverse)
+                    uint8_t* dst = vs + 8 * col * C::VROW + 2 * vt_slot(d);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        *reinterpret_cast<uint16_t*>(dst + 2 * e * C::VROW) = static_cast<uint16_t>(vst[i][e]);
+                        *reinterpret_cast<uint16_t*>(dst + (2 * e + 1) * C::VROW) =
+                            static_cast<uint16_t>(vst[i][e] >> 16);
+                    }
+                } else {
+                    *reinterpret_cast<u32x4*>(vs + d * C::VROW + 16 * col) = vst[i];
+                }
             }
         }
         if constexpr (PV8) {

@@ -58,6 +58,13 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Keys per tile of the bf16/FP8 attention kernel; V^T rows are padded to a multiple of it.
 constexpr int kKeyTile = 64;
 
+// Head sizes from which the bf16/FP8 attention kernel reads V through the V^T
+// workspace of launch_transpose_v; below it the kernel reads V [BH, N, d] as it
+// is and transposes each tile on its way into LDS (the FP8 P*V kernel always
+// reads the e4m3 V^T of launch_quant_v_pow2).
+constexpr int kVtMinD = 128;
+inline bool fwd_reads_vt(int d) { return d >= kVtMinD; }
+
 // Enqueue the merge of n_parts partial results (o_parts [n_parts, BH, N, d]
 // fp32, lse_parts [n_parts, BH, N]) into bf16 o [BH, N, d] and lse (may be null):
 // lse = ln sum_g exp(lse_g), O = sum_g exp(lse_g - lse) O_g.
