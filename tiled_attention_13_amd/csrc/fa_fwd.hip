@@ -171,13 +171,28 @@ __device__ __forceinline__ int f8_slot(int kk) {
 // slot 2t-3) is done by then, and A first reads tile t in slot 2t.  Global
 // loads land in registers two slots before they are written to LDS.
 // ===========================================================================
+// One LDS-DMA instruction: each lane's 16 bytes at global offset voff of the
+// buffer rsrc land at LDS byte lds + 16 * lane.  Issued through inline
+// assembly so that the compiler does not order every LDS read behind every
+// outstanding copy; the kernel waits for its own copies (vmcnt) before the
+// barrier that publishes a tile.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, u32x4 rsrc, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int D, bool CAUSAL, bool FP8, bool PV8 = false>
 struct PPCfg {
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;           // queries per workgroup
     static constexpr int BN = kKeyTile;          // keys per tile
-    static constexpr int STAGES = 3;
+    // d = 128 (bf16 or e4m3 K, bf16 V^T): tiles go global -> LDS directly
+    // (buffer loads to LDS), issued a slot earlier than a register copy would
+    // store them, so the ring has a fourth stage
+    static constexpr bool DMA = !PV8 && D == 128;
+    static constexpr int STAGES = DMA ? 4 : 3;
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
     static constexpr int VES = PV8 ? 1 : 2;      // bytes per V element
@@ -316,7 +331,63 @@ void fwd_pp_kernel(KParams p) {
     // valid bytes live in scalar registers, each thread's offset within the tile
     // is fixed, and rows past the end of the sequence read as zero (the hardware
     // range check), so full and partial tiles share one path.
+    // DMA path: a stage is BN K rows (KROW-byte stride: D*ES/16 granules of 16
+    // bytes + one pad granule) then D V^T rows (VROW: 8 + 1 granules), i.e.
+    // DMA_ALL contiguous 1 KiB blocks, one LDS-DMA instruction each; group A
+    // copies the first DMA_A blocks, group B the rest, block b of a group by
+    // its wave b mod 4.  A lane that falls on a pad granule reads past the
+    // buffer (zero, no memory traffic).
+    constexpr int DMA_K = C::KBYTES / 1024, DMA_ALL = (C::KBYTES + C::VBYTES) / 1024;
+    constexpr int DMA_A = (DMA_ALL + 1) / 2, DMA_PER_W = (DMA_A + 3) / 4;
+    constexpr int KG = C::KROW / 16, KD = D * ES / 16, VG = C::VROW / 16, VD = BN * 2 / 16;
+    uint32_t dma_off[DMA_PER_W];
+    int dma_n = 0;
+    uint32_t smem_lds = 0;
+    if constexpr (C::DMA) {
+        static_assert(C::KBYTES % 1024 == 0 && C::VBYTES % 1024 == 0 && KG == KD + 1 && VG == VD + 1 &&
+                      C::SBYTES == 0, "LDS-DMA layout");
+        smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) uint8_t*)smem));
+        const int b0 = grp == 0 ? 0 : DMA_A, b1 = grp == 0 ? DMA_A : DMA_ALL;
+#pragma unroll
+        for (int i = 0; i < DMA_PER_W; ++i) {
+            const int b = b0 + (w & 3) + 4 * i;
+            uint32_t off = 0x40000000u;
+            if (b < b1) {
+                if (b < DMA_K) {
+                    const int g = 64 * b + lane, row = g / KG, col = g - KG * row;
+                    if (col < KD) off = row * (D * ES) + 16 * col;
+                } else {
+                    const int g = 64 * (b - DMA_K) + lane, row = g / VG, col = g - VG * row;
+                    if (col < VD) off = static_cast<uint32_t>(row) * p.np * 2 + 16 * col;
+                }
+                dma_n = i + 1;
+            }
+            dma_off[i] = off;
+        }
+    }
+    auto dma_tile = [&](int t) {
+        const int n0 = tile_of(t) * BN;
+        const uint64_t ka = reinterpret_cast<uint64_t>(kg + static_cast<size_t>(n0) * D * ES);
+        const uint64_t va = reinterpret_cast<uint64_t>(vtg + static_cast<size_t>(n0) * 2);
+        const u32x4 kr = {static_cast<uint32_t>(ka), static_cast<uint32_t>(ka >> 32) & 0xFFFFu,
+                          static_cast<uint32_t>(min(N - n0, BN) * D * ES), static_cast<uint32_t>(kBufferFlags)};
+        const u32x4 vr = {static_cast<uint32_t>(va), static_cast<uint32_t>(va >> 32) & 0xFFFFu,
+                          (static_cast<uint32_t>(D) * p.np - n0) * 2, static_cast<uint32_t>(kBufferFlags)};
+        const uint32_t stage = smem_lds + (t % C::STAGES) * C::STAGE;
+        const int b0 = (grp == 0 ? 0 : DMA_A) + (w & 3);
+#pragma unroll
+        for (int i = 0; i < DMA_PER_W; ++i) {
+            if (i < dma_n) {
+                const int b = b0 + 4 * i;
+                lds_dma16(stage + 1024 * b, b < DMA_K ? kr : vr, dma_off[i]);
+            }
+        }
+    };
     auto load_tile = [&](int t) {
+        if constexpr (C::DMA) {
+            dma_tile(t);
+            return;
+        }
         const int n0 = tile_of(t) * BN;
         // (byte counts fit 32 bits: B*H*N*d < 2^31 elements of at most 2 bytes)
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
@@ -353,6 +424,10 @@ void fwd_pp_kernel(KParams p) {
         }
     };
     auto store_tile = [&](int t) {
+        if constexpr (C::DMA) {
+            wait_lds_dma();
+            return;
+        }
         uint8_t* ks = smem + (t % C::STAGES) * C::STAGE;
         uint8_t* vs = ks + C::KBYTES;
 #pragma unroll
@@ -611,6 +686,7 @@ void fwd_pp_kernel(KParams p) {
         }
     }
     if (grp == 0) lds_barrier();                  // group A idles through the last slot
+    if constexpr (C::DMA) wait_lds_dma();         // no copy may land after the workgroup ends
 
     // ---- epilogue
     const float l_tot = sum_halves(l_run);
