@@ -188,10 +188,10 @@ struct PPCfg {
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;           // queries per workgroup
     static constexpr int BN = kKeyTile;          // keys per tile
-    // d = 128 (bf16 or e4m3 K, bf16 V^T): tiles go global -> LDS directly
-    // (buffer loads to LDS), issued a slot earlier than a register copy would
-    // store them, so the ring has a fourth stage
-    static constexpr bool DMA = !PV8 && D == 128;
+    // d = 128: K and V^T tiles go global -> LDS directly (buffer loads to LDS),
+    // issued a slot earlier than a register copy would store them, so the ring
+    // has a fourth stage
+    static constexpr bool DMA = D == 128;
     static constexpr int STAGES = DMA ? 4 : 3;
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
@@ -332,20 +332,21 @@ void fwd_pp_kernel(KParams p) {
     // is fixed, and rows past the end of the sequence read as zero (the hardware
     // range check), so full and partial tiles share one path.
     // DMA path: a stage is BN K rows (KROW-byte stride: D*ES/16 granules of 16
-    // bytes + one pad granule) then D V^T rows (VROW: 8 + 1 granules), i.e.
-    // DMA_ALL contiguous 1 KiB blocks, one LDS-DMA instruction each; group A
-    // copies the first DMA_A blocks, group B the rest, block b of a group by
+    // bytes + one pad granule) then D V^T rows (VROW: BN*VES/16 + 1 granules),
+    // i.e. DMA_ALL contiguous 1 KiB blocks, one LDS-DMA instruction each; group
+    // A copies the first DMA_A blocks, group B the rest, block b of a group by
     // its wave b mod 4.  A lane that falls on a pad granule reads past the
-    // buffer (zero, no memory traffic).
+    // buffer (zero, no memory traffic).  The FP8 P*V block exponents after them
+    // still go through registers.
     constexpr int DMA_K = C::KBYTES / 1024, DMA_ALL = (C::KBYTES + C::VBYTES) / 1024;
     constexpr int DMA_A = (DMA_ALL + 1) / 2, DMA_PER_W = (DMA_A + 3) / 4;
-    constexpr int KG = C::KROW / 16, KD = D * ES / 16, VG = C::VROW / 16, VD = BN * 2 / 16;
+    constexpr int KG = C::KROW / 16, KD = D * ES / 16, VG = C::VROW / 16, VD = BN * C::VES / 16;
     uint32_t dma_off[DMA_PER_W];
     int dma_n = 0;
     uint32_t smem_lds = 0;
     if constexpr (C::DMA) {
-        static_assert(C::KBYTES % 1024 == 0 && C::VBYTES % 1024 == 0 && KG == KD + 1 && VG == VD + 1 &&
-                      C::SBYTES == 0, "LDS-DMA layout");
+        static_assert(C::KBYTES % 1024 == 0 && C::VBYTES % 1024 == 0 && KG == KD + 1 && VG == VD + 1,
+                      "LDS-DMA layout");
         smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) uint8_t*)smem));
         const int b0 = grp == 0 ? 0 : DMA_A, b1 = grp == 0 ? DMA_A : DMA_ALL;
 #pragma unroll
@@ -358,7 +359,7 @@ void fwd_pp_kernel(KParams p) {
                     if (col < KD) off = row * (D * ES) + 16 * col;
                 } else {
                     const int g = 64 * (b - DMA_K) + lane, row = g / VG, col = g - VG * row;
-                    if (col < VD) off = static_cast<uint32_t>(row) * p.np * 2 + 16 * col;
+                    if (col < VD) off = static_cast<uint32_t>(row) * p.np * C::VES + 16 * col;
                 }
                 dma_n = i + 1;
             }
@@ -368,11 +369,11 @@ void fwd_pp_kernel(KParams p) {
     auto dma_tile = [&](int t) {
         const int n0 = tile_of(t) * BN;
         const uint64_t ka = reinterpret_cast<uint64_t>(kg + static_cast<size_t>(n0) * D * ES);
-        const uint64_t va = reinterpret_cast<uint64_t>(vtg + static_cast<size_t>(n0) * 2);
+        const uint64_t va = reinterpret_cast<uint64_t>(vtg + static_cast<size_t>(n0) * C::VES);
         const u32x4 kr = {static_cast<uint32_t>(ka), static_cast<uint32_t>(ka >> 32) & 0xFFFFu,
                           static_cast<uint32_t>(min(N - n0, BN) * D * ES), static_cast<uint32_t>(kBufferFlags)};
         const u32x4 vr = {static_cast<uint32_t>(va), static_cast<uint32_t>(va >> 32) & 0xFFFFu,
-                          (static_cast<uint32_t>(D) * p.np - n0) * 2, static_cast<uint32_t>(kBufferFlags)};
+                          (static_cast<uint32_t>(D) * p.np - n0) * C::VES, static_cast<uint32_t>(kBufferFlags)};
         const uint32_t stage = smem_lds + (t % C::STAGES) * C::STAGE;
         const int b0 = (grp == 0 ? 0 : DMA_A) + (w & 3);
 #pragma unroll
@@ -386,6 +387,10 @@ void fwd_pp_kernel(KParams p) {
     auto load_tile = [&](int t) {
         if constexpr (C::DMA) {
             dma_tile(t);
+            if constexpr (PV8) {
+                if (tid < C::SBYTES / 16)
+                    sst = ld16(p.vscale + (static_cast<size_t>(bh) * n_all_tiles + tile_of(t)) * D + 16 * tid);
+            }
             return;
         }
         const int n0 = tile_of(t) * BN;
@@ -426,6 +431,10 @@ void fwd_pp_kernel(KParams p) {
     auto store_tile = [&](int t) {
         if constexpr (C::DMA) {
             wait_lds_dma();
+            if constexpr (PV8) {
+                if (tid < C::SBYTES / 16)
+                    *reinterpret_cast<u32x4*>(smem + (t % C::STAGES) * C::STAGE + C::KBYTES + C::VBYTES + 16 * tid) = sst;
+            }
             return;
         }
         uint8_t* ks = smem + (t % C::STAGES) * C::STAGE;
