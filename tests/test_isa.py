@@ -1,11 +1,11 @@
-"""Checks on the gfx950 ISA of the forward kernels (CPU only: hipcc cross-compiles).
+"""Checks on the gfx950 ISA of the attention kernels (CPU only: hipcc cross-compiles).
 
-The d = 128 kernels copy tiles with LDS-DMA instructions written as inline
-assembly that set M0 themselves.  The compiler treats M0 as reserved and does
+The d = 128 forward kernels and the backward kernels copy tiles with LDS-DMA
+instructions written as inline assembly that set M0 themselves.  The compiler treats M0 as reserved and does
 not save it around inline assembly, so the kernels are only correct while
 nothing else in them reads or writes M0: every M0 write must be one of those
 copies (``s_mov_b32 m0, sN`` directly followed by the buffer load to LDS).
-The forward kernels must also keep every value in registers (no scratch).
+The kernels must also keep every value in registers (no scratch).
 """
 from __future__ import annotations
 
@@ -20,23 +20,23 @@ from tiled_attention_13_amd import build as fa_build
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-@pytest.fixture(scope="module")
-def fwd_isa(tmp_path_factory):
+@pytest.fixture(scope="module", params=["fa_fwd.hip", "fa_bwd.hip"])
+def isa(request, tmp_path_factory):
     try:
         cc = fa_build.hipcc()
     except RuntimeError:
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "fa_fwd.s"
+    out = tmp_path_factory.mktemp("isa") / (request.param + ".s")
     flags = [f for f in fa_build.HIP_FLAGS if f != "-fPIC"]
     cmd = [cc, *flags, "--cuda-device-only", "-S", "-I", fa_build.INCLUDE, "-I", fa_build.CSRC,
-           os.path.join(fa_build.CSRC, "fa_fwd.hip"), "-o", str(out)]
+           os.path.join(fa_build.CSRC, request.param), "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return out.read_text().splitlines()
 
 
-def test_m0_only_set_by_tile_copies(fwd_isa):
-    lines = [l.strip() for l in fwd_isa]
+def test_m0_only_set_by_tile_copies(isa):
+    lines = [l.strip() for l in isa]
     copies = 0
     for i, l in enumerate(lines):
         if l.startswith(";") or not re.search(r"\bm0\b", l):
@@ -48,12 +48,12 @@ def test_m0_only_set_by_tile_copies(fwd_isa):
     assert copies > 0, "no LDS-DMA tile copies found"
 
 
-def test_forward_kernels_use_no_scratch(fwd_isa):
+def test_attention_kernels_use_no_scratch(isa):
     sizes = {}
-    for l in fwd_isa:
-        m = re.match(r"\s*\.set (_ZN\S*fwd_pp_kernel\S*)\.private_seg_size, (\d+)", l)
+    for l in isa:
+        m = re.match(r"\s*\.set (_ZN\S*(?:fwd_pp_kernel|bwd_kv_kernel|bwd_dq_kernel)\S*)\.private_seg_size, (\d+)", l)
         if m:
             sizes[m.group(1)] = int(m.group(2))
-    assert sizes, "no forward kernel instances found"
+    assert sizes, "no attention kernel instances found"
     spilled = {k: v for k, v in sizes.items() if v}
     assert not spilled, f"scratch in {spilled}"

@@ -104,15 +104,9 @@ struct DqCfg {
     static constexpr int BN = kKeyTile;
     static constexpr int KROW = 2 * D + 16;              // bytes per K / V row in LDS (padded)
     static constexpr int TROW = 2 * BN + 16;             // bytes per K^T row in LDS (padded)
-    static constexpr int KBYTES = BN * KROW;
-    static constexpr int TBYTES = D * TROW;
+    static constexpr int KBYTES = dma_region_bytes(BN * KROW);
+    static constexpr int TBYTES = dma_region_bytes(D * TROW);
     static constexpr int STAGE = 2 * KBYTES + TBYTES;
-    static constexpr int R_CPR = D / 8;                  // 16-byte chunks per K / V row
-    static constexpr int R_CHUNKS = BN * R_CPR;
-    static constexpr int T_CPR = 2 * BN / 16;            // 16-byte chunks per K^T row
-    static constexpr int T_CHUNKS = D * T_CPR;
-    static constexpr int R_PER_T = (R_CHUNKS + NT - 1) / NT;
-    static constexpr int T_PER_T = (T_CHUNKS + NT - 1) / NT;
     static constexpr int QREGS = D / 16;
 };
 
@@ -157,58 +151,38 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
     const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
     const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
 
-    // A tile is copied in two halves of 32 keys (K and V rows, and the matching
-    // 32 key slots of every K^T row), each loaded just before one 32-key block of
-    // the current tile is computed and written to LDS right after it.  Buffer
-    // loads: rows past the end of the sequence read as zero.
-    constexpr int HR = C::R_CHUNKS / 2, HT = C::T_CHUNKS / 2;      // chunks per half
-    constexpr int HR_PER_T = (HR + NT - 1) / NT, HT_PER_T = (HT + NT - 1) / NT;
-    u32x4 kst[HR_PER_T], vst[HR_PER_T], tst[HT_PER_T];
-    auto load_half = [&](int t, int half) {
-        const int n0 = t * BN + 32 * half;
-        const int valid = max(0, min(N - n0, 32)) * D * 2;
-        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(kg + static_cast<size_t>(min(n0, N)) * D * 2), 0, valid, kBufferFlags);
-        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(vg + static_cast<size_t>(min(n0, N)) * D * 2), 0, valid, kBufferFlags);
+    // Tiles go global -> LDS directly (buffer loads to LDS): a stage is K rows,
+    // V rows (272-byte stride: 16 granules + one pad) and K^T rows (144 bytes:
+    // 8 + 1), NB contiguous 1 KiB blocks, block b copied by wave b mod 8.  The
+    // copy of tile j+1 is issued before tile j is computed and waited for
+    // before the barrier that ends it; the hardware range check zero-fills
+    // keys past the end of the sequence.
+    static_assert(C::KROW == 2 * D + 16 && C::TROW == 144, "LDS-DMA layout");
+    constexpr int NB_K = C::KBYTES / 1024, NB = 2 * NB_K + C::TBYTES / 1024, PER_W = (NB + 7) / 8;
+    uint32_t doff[PER_W];
+    int dn = 0;
 #pragma unroll
-        for (int i = 0; i < HR_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < HR) {
-                const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                kst[i] = __builtin_amdgcn_raw_buffer_load_b128(kr, row * D * 2 + 16 * col, 0, 0);
-                vst[i] = __builtin_amdgcn_raw_buffer_load_b128(vr, row * D * 2 + 16 * col, 0, 0);
-            }
+    for (int i = 0; i < PER_W; ++i) {
+        const int b = w + 8 * i;
+        doff[i] = 0x40000000u;
+        if (b < NB) {
+            doff[i] = b < 2 * NB_K ? dma_lane_offset(b % NB_K, lane, D / 8, D * 2, BN)
+                                   : dma_lane_offset(b - 2 * NB_K, lane, BN / 8, p.np * 2, D);
+            dn = i + 1;
         }
+    }
+    const uint32_t smem_lds = lds_address(smem);
+    auto copy_tile = [&](int t) {
+        const int n0 = t * BN;
+        const uint32_t valid = static_cast<uint32_t>(min(N - n0, BN)) * D * 2;
+        const u32x4 kr = buffer_words(kg + static_cast<size_t>(n0) * D * 2, valid);
+        const u32x4 vr = buffer_words(vg + static_cast<size_t>(n0) * D * 2, valid);
+        const u32x4 tr = buffer_words(ktg + static_cast<size_t>(n0) * 2, (static_cast<uint32_t>(D) * p.np - n0) * 2);
+        const uint32_t stage = smem_lds + (t & 1) * C::STAGE;
 #pragma unroll
-        for (int i = 0; i < HT_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < HT) {
-                const int d = c / (C::T_CPR / 2), col = c - d * (C::T_CPR / 2) + half * (C::T_CPR / 2);
-                tst[i] = ld16(ktg + (static_cast<size_t>(d) * p.np + t * BN) * 2 + 16 * col);
-            }
-        }
-    };
-    auto store_half = [&](int t, int half) {
-        uint8_t* ks = smem + (t & 1) * C::STAGE;
-        uint8_t* vs = ks + C::KBYTES;
-        uint8_t* ts = vs + C::KBYTES;
-#pragma unroll
-        for (int i = 0; i < HR_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < HR) {
-                const int row = c / C::R_CPR + 32 * half, col = c - (c / C::R_CPR) * C::R_CPR;
-                *reinterpret_cast<u32x4*>(ks + row * C::KROW + 16 * col) = kst[i];
-                *reinterpret_cast<u32x4*>(vs + row * C::KROW + 16 * col) = vst[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < HT_PER_T; ++i) {
-            const int c = i * NT + tid;
-            if (c < HT) {
-                const int d = c / (C::T_CPR / 2), col = c - d * (C::T_CPR / 2) + half * (C::T_CPR / 2);
-                *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
-            }
+        for (int i = 0; i < PER_W; ++i) {
+            const int b = w + 8 * i;
+            if (i < dn) lds_dma16(stage + 1024 * b, b < NB_K ? kr : (b < 2 * NB_K ? vr : tr), doff[i]);
         }
     };
 
@@ -263,21 +237,15 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
         compute(j, kb, j == j_last && ((CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N));
     };
 
-    load_half(0, 0);
-    store_half(0, 0);
-    load_half(0, 1);
-    store_half(0, 1);
+    copy_tile(0);
+    wait_lds_dma();
     __syncthreads();
     for (int j = 0; j < n_kt; ++j) {
         const bool more = j + 1 < n_kt;
-        if (more) load_half(j + 1, 0);
+        if (more) copy_tile(j + 1);
         compute_block(j, 0);
-        if (more) {
-            store_half(j + 1, 0);
-            load_half(j + 1, 1);
-        }
         compute_block(j, 1);
-        if (more) store_half(j + 1, 1);
+        if (more) wait_lds_dma();
         __syncthreads();
     }
 
@@ -312,19 +280,13 @@ struct KvCfg {
     static constexpr int BQ = 64;                        // queries per tile
     static constexpr int RROW = 2 * D + 16;              // bytes per Q / dO row in LDS (padded)
     static constexpr int TROW = 2 * BQ + 16;             // bytes per dO^T / Q^T row in LDS (padded)
-    static constexpr int RBYTES = BQ * RROW;
-    static constexpr int TBYTES = D * TROW;
+    static constexpr int RBYTES = dma_region_bytes(BQ * RROW);
+    static constexpr int TBYTES = dma_region_bytes(D * TROW);
     static constexpr int NR = WHICH == 0 ? 1 : 2;        // row-major tiles: Q (and dO)
     static constexpr int VEC = BQ * 4;
     static constexpr int NV = WHICH == 0 ? 1 : 2;        // row vectors: lse2 (and D)
     static constexpr int STAGE = NR * RBYTES + TBYTES + NV * VEC;
-    static constexpr int R_CPR = D / 8;
-    static constexpr int R_CHUNKS = BQ * R_CPR;
-    static constexpr int T_CPR = 2 * BQ / 16;
-    static constexpr int T_CHUNKS = D * T_CPR;
     static constexpr int V_CHUNKS = NV * VEC / 16;
-    static constexpr int R_PER_T = (R_CHUNKS + NT - 1) / NT;
-    static constexpr int T_PER_T = (T_CHUNKS + NT - 1) / NT;
     static constexpr int QREGS = D / 16;
 };
 
@@ -365,39 +327,44 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
     const int t0 = CAUSAL ? min(k0 / BQ, n_qt) : 0;
     const int t_first = CAUSAL ? max(t0, kw0 / BQ) : 0;  // first tile with a query at or after this wave's keys
 
-    // Tile copy in two parts around the two 32-query blocks of the current
-    // tile (part 0: Q rows and the row vectors; part 1: the transposed tile and,
-    // for dK, the dO rows), through buffer loads whose range check zero-fills
-    // rows past the end of the sequence.
-    u32x4 rst[C::R_PER_T], tst[C::T_PER_T], vecst;
-    auto load_part = [&](int t, int part) {
+    // Tiles go global -> LDS directly (buffer loads to LDS): a stage is Q rows
+    // (and dO rows) at a 272-byte stride (16 granules + one pad), then the
+    // transposed tile at 144 bytes (8 + 1), NB contiguous 1 KiB blocks, block b
+    // copied by wave b mod 8; the hardware range check zero-fills rows past
+    // the end of the sequence.  The row vectors (lse2, and D) follow through
+    // registers: rows past the end get lse2 = +inf (P = 0) and D = 0.
+    static_assert(C::RROW == 2 * D + 16 && C::TROW == 144, "LDS-DMA layout");
+    constexpr int NB_R = C::RBYTES / 1024, NB = C::NR * NB_R + C::TBYTES / 1024, PER_W = (NB + 7) / 8;
+    uint32_t doff[PER_W];
+    int dn = 0;
+#pragma unroll
+    for (int i = 0; i < PER_W; ++i) {
+        const int b = w + 8 * i;
+        doff[i] = 0x40000000u;
+        if (b < NB) {
+            doff[i] = b < C::NR * NB_R ? dma_lane_offset(b % NB_R, lane, D / 8, D * 2, BQ)
+                                       : dma_lane_offset(b - C::NR * NB_R, lane, BQ / 8, p.np * 2, D);
+            dn = i + 1;
+        }
+    }
+    const uint32_t smem_lds = lds_address(smem);
+    auto copy_tile = [&](int t) {
         const int m0 = t * BQ;
-        const int valid = min(N - m0, BQ) * D * 2;
-        if (part == 0 || WHICH == 1) {
-            const uint8_t* rg = part == 0 ? qg : gg;
-            const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint8_t*>(rg + static_cast<size_t>(m0) * D * 2), 0, valid, kBufferFlags);
+        const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ)) * D * 2;
+        const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid);
+        const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid);
+        const u32x4 rt = buffer_words(tg + static_cast<size_t>(m0) * 2, (static_cast<uint32_t>(D) * p.np - m0) * 2);
+        const uint32_t stage = smem_lds + (t & 1) * C::STAGE;
 #pragma unroll
-            for (int i = 0; i < C::R_PER_T; ++i) {
-                const int c = i * NT + tid;
-                if (c < C::R_CHUNKS) {
-                    const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                    rst[i] = __builtin_amdgcn_raw_buffer_load_b128(rr, row * D * 2 + 16 * col, 0, 0);
-                }
-            }
+        for (int i = 0; i < PER_W; ++i) {
+            const int b = w + 8 * i;
+            if (i < dn) lds_dma16(stage + 1024 * b, b < NB_R ? rq : (b < C::NR * NB_R ? rg : rt), doff[i]);
         }
-        if (part == 1) {
-#pragma unroll
-            for (int i = 0; i < C::T_PER_T; ++i) {
-                const int c = i * NT + tid;
-                if (c < C::T_CHUNKS) {
-                    const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                    tst[i] = ld16(tg + (static_cast<size_t>(d) * p.np + m0) * 2 + 16 * col);
-                }
-            }
-        }
-        if (part == 0 && tid < C::V_CHUNKS) {
-            // 4 rows per chunk; rows past the end get lse2 = +inf (P = 0) and D = 0
+    };
+    u32x4 vecst;
+    auto load_vec = [&](int t) {
+        if (tid < C::V_CHUNKS) {
+            const int m0 = t * BQ;
             const int which = tid / (C::VEC / 16), r0 = m0 + 4 * (tid - which * (C::VEC / 16));
             const float* src = which == 0 ? l2g : dsg;
             const float fill = which == 0 ? __builtin_inff() : 0.0f;
@@ -405,32 +372,9 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
             for (int e = 0; e < 4; ++e) vecst[e] = __float_as_uint(r0 + e < N ? src[r0 + e] : fill);
         }
     };
-    auto store_part = [&](int t, int part) {
-        uint8_t* stage = smem + (t & 1) * C::STAGE;
-        if (part == 0 || WHICH == 1) {
-            uint8_t* rs = stage + part * C::RBYTES;
-#pragma unroll
-            for (int i = 0; i < C::R_PER_T; ++i) {
-                const int c = i * NT + tid;
-                if (c < C::R_CHUNKS) {
-                    const int row = c / C::R_CPR, col = c - row * C::R_CPR;
-                    *reinterpret_cast<u32x4*>(rs + row * C::RROW + 16 * col) = rst[i];
-                }
-            }
-        }
-        if (part == 1) {
-            uint8_t* ts = stage + C::NR * C::RBYTES;
-#pragma unroll
-            for (int i = 0; i < C::T_PER_T; ++i) {
-                const int c = i * NT + tid;
-                if (c < C::T_CHUNKS) {
-                    const int d = c / C::T_CPR, col = c - d * C::T_CPR;
-                    *reinterpret_cast<u32x4*>(ts + d * C::TROW + 16 * col) = tst[i];
-                }
-            }
-        }
-        if (part == 0 && tid < C::V_CHUNKS)
-            *reinterpret_cast<u32x4*>(stage + C::NR * C::RBYTES + C::TBYTES + 16 * tid) = vecst;
+    auto store_vec = [&](int t) {
+        if (tid < C::V_CHUNKS)
+            *reinterpret_cast<u32x4*>(smem + (t & 1) * C::STAGE + C::NR * C::RBYTES + C::TBYTES + 16 * tid) = vecst;
     };
 
     f32x16 acc[D / 32];
@@ -491,22 +435,24 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
     };
 
     if (t0 < n_qt) {
-        load_part(t0, 0);
-        store_part(t0, 0);
-        load_part(t0, 1);
-        store_part(t0, 1);
+        copy_tile(t0);
+        load_vec(t0);
+        store_vec(t0);
+        wait_lds_dma();
     }
     __syncthreads();
     for (int t = t0; t < n_qt; ++t) {
         const bool more = t + 1 < n_qt;
-        if (more) load_part(t + 1, 0);
-        compute_block(t, 0);
         if (more) {
-            store_part(t + 1, 0);
-            load_part(t + 1, 1);
+            copy_tile(t + 1);
+            load_vec(t + 1);
         }
+        compute_block(t, 0);
         compute_block(t, 1);
-        if (more) store_part(t + 1, 1);
+        if (more) {
+            store_vec(t + 1);
+            wait_lds_dma();
+        }
         __syncthreads();
     }
 

@@ -76,5 +76,41 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// One LDS-DMA instruction: each lane's 16 bytes at global offset voff of the
+// buffer rsrc land at LDS byte lds + 16 * lane.  Issued through inline
+// assembly so that the compiler does not order every LDS read behind every
+// outstanding copy; the kernel waits for its own copies (vmcnt) before the
+// barrier that publishes a tile.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, u32x4 rsrc, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds), "v"(voff), "s"(rsrc)
+                 : "memory");
+}
+__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Buffer resource words for a byte range [base, base + bytes) (the layout
+// __builtin_amdgcn_make_buffer_rsrc builds), for the inline-assembly copies.
+__device__ __forceinline__ u32x4 buffer_words(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xFFFFu, bytes,
+                 static_cast<uint32_t>(kBufferFlags)};
+}
+
+// LDS byte address of a __shared__ object (what M0 takes).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const uint8_t*)p));
+}
+
+// Per-lane global offset of 1 KiB LDS block b of a region of `rows` padded
+// rows: row r of the region holds `data` 16-byte granules of global row r
+// (global row stride `stride` bytes) followed by one pad granule.  A lane on a
+// pad granule or past the last row gets an offset past any buffer (it reads
+// zero and moves no data).
+__device__ __forceinline__ uint32_t dma_lane_offset(int b, int lane, int data, uint32_t stride, int rows) {
+    const int g = 64 * b + lane, row = g / (data + 1), col = g - (data + 1) * row;
+    return col < data && row < rows ? static_cast<uint32_t>(row) * stride + 16 * col : 0x40000000u;
+}
+
+// Bytes of LDS a region of padded rows occupies: whole 1 KiB copy blocks.
+constexpr int dma_region_bytes(int bytes) { return (bytes + 1023) / 1024 * 1024; }
 }  // namespace
 }  // namespace fa

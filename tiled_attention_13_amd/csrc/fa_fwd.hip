@@ -171,16 +171,6 @@ __device__ __forceinline__ int f8_slot(int kk) {
 // slot 2t-3) is done by then, and A first reads tile t in slot 2t.  Global
 // loads land in registers two slots before they are written to LDS.
 // ===========================================================================
-// One LDS-DMA instruction: each lane's 16 bytes at global offset voff of the
-// buffer rsrc land at LDS byte lds + 16 * lane.  Issued through inline
-// assembly so that the compiler does not order every LDS read behind every
-// outstanding copy; the kernel waits for its own copies (vmcnt) before the
-// barrier that publishes a tile.
-__device__ __forceinline__ void lds_dma16(uint32_t lds, u32x4 rsrc, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory");
-}
-__device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int D, bool CAUSAL, bool FP8, bool PV8 = false>
 struct PPCfg {
