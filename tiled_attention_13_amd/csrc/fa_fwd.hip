@@ -172,7 +172,7 @@ __device__ __forceinline__ int f8_slot(int kk) {
 // loads land in registers two slots before they are written to LDS.
 // ===========================================================================
 
-template <int D, bool CAUSAL, bool FP8, bool PV8 = false>
+template <int D, bool CAUSAL, bool FP8, bool PV8 = false, int MODE = kModeDense>
 struct PPCfg {
     static constexpr int NW = 8;
     static constexpr int NT = 64 * NW;
@@ -180,8 +180,9 @@ struct PPCfg {
     static constexpr int BN = kKeyTile;          // keys per tile
     // d = 128: K and V^T tiles go global -> LDS directly (buffer loads to LDS),
     // issued a slot earlier than a register copy would store them, so the ring
-    // has a fourth stage
-    static constexpr bool DMA = D == 128;
+    // has a fourth stage.  Not in the block-sparse kernel: its short runs of
+    // listed tiles measured slower that way.
+    static constexpr bool DMA = D == 128 && MODE != kModeSparse;
     static constexpr int STAGES = DMA ? 4 : 3;
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
@@ -211,7 +212,7 @@ struct PPCfg {
 template <int D, bool CAUSAL, bool FP8, int MODE, bool PV8 = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((D < 128 && MODE == kModeDense) ? 4 : 2)))
 void fwd_pp_kernel(KParams p) {
-    using C = PPCfg<D, CAUSAL, FP8, PV8>;
+    using C = PPCfg<D, CAUSAL, FP8, PV8, MODE>;
     constexpr bool PARTIAL = MODE == kModePartial, SPARSE = MODE == kModeSparse;
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT, ES = C::ES;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE];
