@@ -197,11 +197,12 @@ def _time_cold(fn, steps: int, flush) -> np.ndarray:
     return np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
 
 
-# VALU estimate for the small-d shapes: per score about four full-rate VALU
+# VALU floor for the small-d shapes: per score about four full-rate VALU
 # instructions (scale-and-subtract FMA, running sum, half a max3, half a
-# bf16 pack) at 4 cycles per wave64 instruction, plus one v_exp_f32 at about
-# 12 cycles, over 256 CUs x 4 SIMDs at 2.4 GHz.
-VALU_CYCLES_PER_SCORE = (4 * 4 + 12) / 64.0
+# bf16 pack) at 2 cycles per wave64 instruction and one v_exp_f32 at about 6
+# (issue rates measured with a probe of independent chains), over 256 CUs x 4
+# SIMDs at 2.4 GHz.
+VALU_CYCLES_PER_SCORE = (4 * 2 + 6) / 64.0
 N_SIMD = 256 * 4
 CLOCK_HZ = 2.4e9
 
@@ -236,9 +237,17 @@ def bench_configs(flush_mib: int = 512):
             r["hbm_gbps_cold"] = round(w.compulsory_bytes() / cmed / 1e6, 1)
             r["pct_hbm_peak_cold"] = round(100.0 * w.compulsory_bytes() / cmed / 1e6 / PEAK_HBM_GBPS, 2)
         if w.d <= 64 and w.dtype == "bf16":
+            # floors: vector ALU work, compulsory HBM bytes, matrix-core FLOPs; when the call
+            # takes more than twice the largest, none of them binds (each workgroup's
+            # sequential walk over its key tiles does)
             scores = w.B * w.H * float(w.N) ** 2 * (0.5 if w.causal else 1.0)
-            r["valu_estimate_ms"] = round(scores * VALU_CYCLES_PER_SCORE / N_SIMD / CLOCK_HZ * 1e3, 4)
-            r["bound"] = "valu"
+            floors = {"valu": scores * VALU_CYCLES_PER_SCORE / N_SIMD / CLOCK_HZ * 1e3,
+                      "hbm": w.compulsory_bytes() / (PEAK_HBM_GBPS * 1e6),
+                      "mfma": w.flops() / (PEAK_TFLOPS[w.dtype] * 1e9)}
+            r["floors_ms"] = {k: round(x, 4) for k, x in floors.items()}
+            r["valu_estimate_ms"] = r["floors_ms"]["valu"]
+            top = max(floors, key=floors.get)
+            r["bound"] = top if med <= 2.0 * floors[top] else "latency"
         elif w.dtype == "f32":
             r["bound"] = "launch latency"
         else:
