@@ -58,3 +58,26 @@ def test_long_single_head_backward(gpu_lib):
         err = np.abs(got - ref)
         bound = 2e-2 * max(np.abs(ref).max(), 1e-3) + 2.0 ** -8 * np.abs(ref)
         assert np.all(err <= bound), (name, float(err.max()), float(np.abs(ref).max()))
+
+
+@pytest.mark.parametrize("name,n_prefix", [("c4_bf16", 12345), ("c5_fp8", 20032), ("c5_fp8pv", 20032)])
+def test_causal_prefix_invariant_full_size(gpu_lib, name, n_prefix):
+    """Causal attention of rows [0, n) depends only on the first n keys: at the
+    workload's full size, in the launch configuration the benchmark times, the
+    first n rows of the output equal the output of the first n rows alone.  The
+    kernels visit the same key tiles in the same order for those rows and keys
+    past a row are masked either way, so the two agree bit for bit (FP8: n is a
+    multiple of the 64-row scale tile, so the codes and scales agree too)."""
+    import torch
+    from tiled_attention_13_amd import fwd
+    from tiled_attention_13_amd.inputs import WORKLOADS
+    w = WORKLOADS[name]
+    q, k, v = make_inputs(w)
+    tq, tk, tv = (to_device(a, "bf16") for a in (q, k, v))
+    o_full, l_full = fwd(tq, tk, tv, causal=True, dtype=w.dtype)
+    pq, pk, pv = (t[:, :, :n_prefix].contiguous() for t in (tq, tk, tv))
+    o_pre, l_pre = fwd(pq, pk, pv, causal=True, dtype=w.dtype)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o_full.float()).all() and torch.isfinite(l_full).all()
+    assert torch.equal(o_full[:, :, :n_prefix], o_pre), name
+    assert torch.equal(l_full[:, :, :n_prefix], l_pre), name
