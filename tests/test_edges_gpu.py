@@ -81,3 +81,38 @@ def test_causal_prefix_invariant_full_size(gpu_lib, name, n_prefix):
     assert torch.isfinite(o_full.float()).all() and torch.isfinite(l_full).all()
     assert torch.equal(o_full[:, :, :n_prefix], o_pre), name
     assert torch.equal(l_full[:, :, :n_prefix], l_pre), name
+
+
+@pytest.mark.parametrize("path", ["bf16", "fp8pv", "bwd", "splitkv", "blocksparse"])
+def test_repeated_runs_bit_identical(gpu_lib, path):
+    """Every kernel that streams tiles through an LDS ring gives the same bits on
+    ten runs of the same input (a race between a tile copy and the reads of the
+    stage it overwrites would show up as run-to-run differences)."""
+    import torch
+    import tiled_attention_13_amd as fa
+    from tiled_attention_13_amd.inputs import random_block_mask
+    w = Workload("rep", 1, 8, 2048 + 37, 128, "bf16", True, 93)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = (to_device(a, "bf16") for a in (q, k, v))
+    if path == "bwd":
+        o, lse = fa.fwd(tq, tk, tv, causal=True)
+        tg = to_device(make_grad(w), "bf16")
+    if path == "blocksparse":
+        nb = (w.N + 63) // 64
+        mask = torch.from_numpy(random_block_mask(nb, 0.4, 94)).to("cuda")
+
+    def run():
+        if path in ("bf16", "fp8pv"):
+            return fa.fwd(tq, tk, tv, causal=True, dtype=path)
+        if path == "bwd":
+            return fa.bwd(tq, tk, tv, o, tg, lse, causal=True)
+        if path == "splitkv":
+            return fa.fwd_splitkv(tq, tk, tv, 3, causal=True)
+        return fa.fwd_blocksparse(tq, tk, tv, mask, causal=True)
+
+    first = [t.clone() for t in run()]
+    for _ in range(9):
+        again = run()
+        torch.cuda.synchronize()
+        for a, b in zip(first, again):
+            assert torch.equal(a, b), path
