@@ -44,6 +44,10 @@
  *   - Arguments are validated before any HIP call, so argument errors are
  *     reported synchronously (also on a machine with no GPU).  No
  *     exceptions, aborts or prints cross this ABI.
+ *   - A call whose stream-ordered workspace cannot be allocated returns
+ *     FA_ERR_OUT_OF_MEMORY having enqueued nothing.  Setting the environment
+ *     variable FA_TEST_FAIL_ALLOC=1 makes every workspace request fail this
+ *     way (read at each call; for tests of that path).
  */
 #ifndef FA_H_
 #define FA_H_

@@ -116,3 +116,39 @@ def test_repeated_runs_bit_identical(gpu_lib, path):
         torch.cuda.synchronize()
         for a, b in zip(first, again):
             assert torch.equal(a, b), path
+
+
+def test_workspace_allocation_failure_is_reported(gpu_lib, monkeypatch):
+    """With FA_TEST_FAIL_ALLOC=1 every entry point that needs a workspace returns
+    FA_ERR_OUT_OF_MEMORY (FAError status 9) and writes nothing; the fp32 forward,
+    which needs none, still runs; afterwards the same calls succeed."""
+    import torch
+    import tiled_attention_13_amd as fa
+    w = Workload("oom", 1, 2, 300, 128, "bf16", True, 95)
+    q, k, v = make_inputs(w)
+    tq, tk, tv = (to_device(a, "bf16") for a in (q, k, v))
+    o, lse = fa.fwd(tq, tk, tv, causal=True)
+    tg = to_device(make_grad(w), "bf16")
+    mask = torch.ones((5, 5), dtype=torch.uint8, device="cuda")
+    calls = {
+        "bf16": lambda out: fa.fwd(tq, tk, tv, causal=True, out=out),
+        "fp8": lambda out: fa.fwd(tq, tk, tv, causal=True, dtype="fp8", out=out),
+        "fp8pv": lambda out: fa.fwd(tq, tk, tv, causal=True, dtype="fp8pv", out=out),
+        "splitkv": lambda out: fa.fwd_splitkv(tq, tk, tv, 2, causal=True, out=out),
+        "blocksparse": lambda out: fa.fwd_blocksparse(tq, tk, tv, mask, causal=True, out=out),
+        "bwd": lambda out: fa.bwd(tq, tk, tv, o, tg, lse, causal=True, dq=out),
+    }
+    monkeypatch.setenv("FA_TEST_FAIL_ALLOC", "1")
+    for name, call in calls.items():
+        out = torch.full_like(tq, 7.0)
+        with pytest.raises(fa.FAError) as e:
+            call(out)
+        assert e.value.status == 9, name
+        torch.cuda.synchronize()
+        assert torch.all(out == 7.0), name                    # nothing was enqueued
+    q32, k32, v32 = (to_device(a, "f32") for a in (q, k, v))
+    fa.fwd(q32, k32, v32, causal=True)                        # no workspace: unaffected
+    monkeypatch.delenv("FA_TEST_FAIL_ALLOC")
+    for name, call in calls.items():
+        call(torch.empty_like(tq))
+    torch.cuda.synchronize()

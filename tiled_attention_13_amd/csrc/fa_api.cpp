@@ -13,6 +13,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "fa_internal.h"
@@ -78,10 +79,14 @@ hipError_t fwd_prepare_v(const void* v, void* vt, int BH, int n, int d, hipStrea
     return fa::fwd_reads_vt(d) ? fa::launch_transpose_v(v, vt, BH, n, d, s) : hipSuccess;
 }
 
-// Stream-ordered workspace; a request of zero bytes allocates nothing.
+// Stream-ordered workspace; a request of zero bytes allocates nothing.  With
+// FA_TEST_FAIL_ALLOC=1 in the environment (read at each call) every request
+// fails as an exhausted device would, so tests can reach the out-of-memory path.
 fa_status ws_alloc(void** p, size_t bytes, hipStream_t s) {
     *p = nullptr;
     if (bytes == 0) return FA_OK;
+    const char* fail = std::getenv("FA_TEST_FAIL_ALLOC");
+    if (fail != nullptr && fail[0] == '1') return FA_ERR_OUT_OF_MEMORY;
     if (hipMallocAsync(p, bytes, s) != hipSuccess || *p == nullptr) {
         (void)hipGetLastError();
         *p = nullptr;
@@ -190,10 +195,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
         const size_t off_ks = off_qs + round_up(n_scales * 4, 256);
         const size_t total = off_ks + round_up(n_scales * 4, 256);
         void* ws = nullptr;
-        if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
-            (void)hipGetLastError();
-            return FA_ERR_OUT_OF_MEMORY;
-        }
+        if ((st = ws_alloc(&ws, total, s)) != FA_OK) return st;
         uint8_t* base = static_cast<uint8_t*>(ws);
         uint8_t* v8 = base + off_v8;
         uint8_t* vs = base + off_vs;
@@ -210,7 +212,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
             a.v_scale = vs;
             e = fa::launch_fwd(a, s);
         }
-        const hipError_t ef = hipFreeAsync(ws, s);
+        const hipError_t ef = ws_free(ws, s);
         if (e != hipSuccess) return launch_status(e);
         return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
     }
@@ -330,10 +332,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
     const size_t off_lse = off_o32 + round_up(static_cast<size_t>(n_splits) * rows * dd * 4, 256);
     const size_t total = off_lse + round_up(static_cast<size_t>(n_splits) * rows * 4, 256);
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
-        (void)hipGetLastError();
-        return FA_ERR_OUT_OF_MEMORY;
-    }
+    if ((st = ws_alloc(&ws, total, s)) != FA_OK) return st;
     uint8_t* base = static_cast<uint8_t*>(ws);
     float* o32 = reinterpret_cast<float*>(base + off_o32);
     float* lse_part = reinterpret_cast<float*>(base + off_lse);
@@ -350,7 +349,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
         e = fa::launch_fwd(a, s);
     }
     if (e == hipSuccess) e = fa::launch_merge(o32, lse_part, static_cast<int>(n_splits), o, lse, BH, n, dd, s);
-    const hipError_t ef = hipFreeAsync(ws, s);
+    const hipError_t ef = ws_free(ws, s);
     if (e != hipSuccess) return launch_status(e);
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -376,10 +375,7 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     const size_t off_cnt = off_list + round_up(n_lists * static_cast<size_t>(nb) * 4, 256);
     const size_t total = off_cnt + round_up(n_lists * 4, 256);
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, total, s) != hipSuccess || ws == nullptr) {
-        (void)hipGetLastError();
-        return FA_ERR_OUT_OF_MEMORY;
-    }
+    if ((st = ws_alloc(&ws, total, s)) != FA_OK) return st;
     uint8_t* base = static_cast<uint8_t*>(ws);
     uint32_t* list = reinterpret_cast<uint32_t*>(base + off_list);
     int* cnt = reinterpret_cast<int*>(base + off_cnt);
@@ -393,7 +389,7 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
         a.bs_stride = static_cast<int>(nb);
         e = fa::launch_fwd(a, s);
     }
-    const hipError_t ef = hipFreeAsync(ws, s);
+    const hipError_t ef = ws_free(ws, s);
     if (e != hipSuccess) return launch_status(e);
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -435,10 +431,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
     const size_t tb = round_up(vt_bytes(BH, n, dd), 256);
     const size_t vec = round_up(static_cast<size_t>(BH) * n * 4, 256);
     void* ws = nullptr;
-    if (hipMallocAsync(&ws, 3 * tb + 2 * vec, s) != hipSuccess || ws == nullptr) {
-        (void)hipGetLastError();
-        return FA_ERR_OUT_OF_MEMORY;
-    }
+    if ((st = ws_alloc(&ws, 3 * tb + 2 * vec, s)) != FA_OK) return st;
     uint8_t* base = static_cast<uint8_t*>(ws);
     void* qt = base;
     void* dot = base + tb;
@@ -453,7 +446,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                       BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
         e = fa::launch_bwd(a, s);
     }
-    const hipError_t ef = hipFreeAsync(ws, s);
+    const hipError_t ef = ws_free(ws, s);
     if (e != hipSuccess) return launch_status(e);
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
