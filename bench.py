@@ -51,7 +51,9 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPS & % MFMA peak (bf16 causal N=16K d=128); ms/call"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp8pv": 5000.0, "f32": 157.3}   # MI355X dense MFMA peaks
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_13_amd", "csrc", f) for f in ("fa_fwd.hip", "fa_api.cpp")]
+# the forward kernel's code: the HBM traffic summary is valid while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_13_amd", "csrc", f)
+                  for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_bf16_traffic.json")
 
 

@@ -66,12 +66,16 @@ typedef enum {
     FA_FP8_E4M3 = 2,  /* q, k, v, o bfloat16 on input; Q and K quantised to
                          e4m3fn per 64-row tile inside the call (see
                          fa_quant_fp8_e4m3), V and P*V stay bf16 */
-    FA_FP8_E4M3_PV = 3 /* as FA_FP8_E4M3, and P*V also on e4m3 matrix cores:
+    FA_FP8_E4M3_PV = 3, /* as FA_FP8_E4M3, and P*V also on e4m3 matrix cores:
                          V quantised per (64-key tile, column) with a
                          power-of-two scale (see fa_quant_v_pow2), P per
                          (query, 64-key tile) with a power-of-two scale
                          inside the kernel; both scales are the MFMA's own
                          block exponents, so dequantisation is exact */
+    /* not dtypes: they widen the enumeration so that any int a caller
+       passes is a valid value of it (reported as FA_ERR_INVALID_DTYPE) */
+    FA_DTYPE_MIN_ENUM = -0x7FFFFFFF - 1,
+    FA_DTYPE_MAX_ENUM = 0x7FFFFFFF
 } fa_dtype;
 
 typedef enum {
@@ -86,7 +90,10 @@ typedef enum {
     FA_ERR_UNSUPPORTED_ARCH = 8,
     FA_ERR_OUT_OF_MEMORY = 9,
     FA_ERR_LAUNCH = 10,
-    FA_ERR_HIP = 11
+    FA_ERR_HIP = 11,
+    /* not statuses: any int is a valid value of the enumeration */
+    FA_STATUS_MIN_ENUM = -0x7FFFFFFF - 1,
+    FA_STATUS_MAX_ENUM = 0x7FFFFFFF
 } fa_status;
 
 /*

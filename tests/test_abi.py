@@ -47,7 +47,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings_cover_every_code(lib):
-    codes = [int(x) for x in re.findall(r"FA_[A-Z0-9_]+\s*=\s*(\d+)", open(HEADER).read())]
+    codes = [int(x) for x in re.findall(r"FA_(?:OK|ERR_[A-Z_]+)\s*=\s*(\d+)", open(HEADER).read())]
     for c in range(max(codes) + 1):
         s = lib.fa_status_string(c).decode()
         assert s and s != "unknown status"

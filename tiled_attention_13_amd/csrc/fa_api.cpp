@@ -33,7 +33,7 @@ fa_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d) {
     // element offsets inside a launch are formed in 32-bit arithmetic per (b, h)
     // slice and 64-bit across slices; keep the whole tensor, with N rounded up
     // to the 64-key tile (the transposed workspaces), below 2^31 elements
-    const long double np = static_cast<long double>((N + 63) / 64 * 64);
+    const long double np = std::ceil(static_cast<long double>(N) / 64.0L) * 64.0L;   // exact for any int64 N
     const long double total = static_cast<long double>(B) * H * np * d;
     if (total >= 2147483648.0L) return FA_ERR_INVALID_SHAPE;
     return FA_OK;
