@@ -41,6 +41,9 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     on it and the call returns without synchronising; faults during
  *     execution surface at the caller's next synchronisation on it.
+ *     A call makes no memset, host read-back or synchronising HIP call, so
+ *     it may be captured into a HIP graph (the workspaces become the
+ *     graph's allocation nodes).
  *   - Arguments are validated before any HIP call, so argument errors are
  *     reported synchronously (also on a machine with no GPU).  No
  *     exceptions, aborts or prints cross this ABI.
