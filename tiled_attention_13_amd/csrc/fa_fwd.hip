@@ -84,9 +84,14 @@ enum : int { kModeDense = 0, kModePartial = 1, kModeSparse = 2 };
 // The reference max only moves when the tile's max exceeds it by more than
 // kRescaleSlack (base-2 units).  Softmax is invariant to the reference, so
 // the result is the same; probabilities are then bounded by 2^kRescaleSlack
-// instead of 1 (harmless in fp32 and bf16), and most tiles need no rescale.
+// instead of 1, and most tiles need no rescale.  bf16 and fp32 keep their
+// relative precision at any exponent; the range bound is the fp32 P*V sum,
+// at most N * 2^45 * max|v|, which stays finite for N * max|v| < 2^82.  (The
+// FP8 P*V path rescales P into the e4m3 range per tile, so it sees the same
+// bound.)  A wide slack matters where a few keys score far above the rest:
+// each new maximum would otherwise cost a rescale of the 64 O accumulators.
 // ---------------------------------------------------------------------------
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kRescaleSlack = 45.0f;
 
 template <int NS>
 __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m, float& l) {
