@@ -63,11 +63,39 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, what="", lse_tol=LSE_TOL):
     return rep
 
 
-def sample_rows(N, seed, n_random=24, block=128):
-    """Query rows to check at full size: ends, tile edges, and random rows."""
+def sample_rows(N, seed, n_random=24, qtile=256):
+    """Query rows to check at full size: ends, the edges of a wave's 32 rows,
+    of a 64-row block and of the kernel's 256-row query tile, and random rows."""
     rng = np.random.default_rng(seed)
-    fixed = [0, 1, 2, 31, 32, 63, 64, block - 1, block, N // 2, N - block - 1, N - block,
+    fixed = [0, 1, 2, 31, 32, 63, 64, 127, 128, qtile - 1, qtile, qtile + 1, N // 2 - 1, N // 2,
+             N - qtile - 1, N - qtile, N - qtile + 1, N - 129, N - 128,
              N - 65, N - 64, N - 33, N - 32, N - 2, N - 1]
     rows = np.concatenate([np.array(fixed), rng.choice(N, n_random, replace=False)])
     rows = rows[(rows >= 0) & (rows < N)]
     return np.unique(rows)
+
+
+def oracle_fp8pv(q, k, v, causal, scale, rows=None):
+    """The oracle on the decoded e4m3 Q, K (per-tile scales) and V (power-of-two
+    scales), and the attention of |V| that bounds the effect of rounding P."""
+    q8, qs = quantize_tiles(q)
+    k8, ks = quantize_tiles(k)
+    v8, ve = oracle.quantize_v_pow2(v)
+    vd = oracle.dequantize_v_pow2(v8, ve)
+    qd, kd = decode_e4m3(q8), decode_e4m3(k8)
+    o, lse = oracle.attention_fp8(qd, qs, kd, ks, vd, causal, scale, rows=rows)
+    a, _ = oracle.attention_fp8(qd, qs, kd, ks, np.abs(vd), causal, scale, rows=rows)
+    return o, lse, a
+
+
+def check_fp8pv(o, lse, o_ref, lse_ref, a, what, lse_tol=LSE_TOL):
+    """|O - O_ref| <= 2^-4 A + 2^-8 |O_ref| + 5e-2 (A: attention of |V|); lse within lse_tol."""
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what
+    err = np.abs(o - o_ref)
+    bound = 2.0 ** -4 * a + 2.0 ** -8 * np.abs(o_ref) + 5e-2
+    if np.any(err > bound):
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {int((err > bound).sum())} elements out of bound; worst {i}: gpu {o[i]:.5g} "
+                             f"ref {o_ref[i]:.5g} bound {bound[i]:.3g}")
+    assert np.abs(lse - lse_ref).max() <= lse_tol, what
+    return float(err.max())

@@ -22,11 +22,57 @@ def test_extreme_softmax_scales(gpu_lib, dtype, scale, causal):
     q, k, v = make_inputs(Workload("e", 1, 2, 700, 64, dtype, False, 90))
     o, lse = gpu_forward(q, k, v, dtype, causal, scale)
     o_ref, lse_ref = oracle_forward(q, k, v, dtype, causal, scale)
-    # the e4m3 MFMA keeps about 14 bits when it sums the products of a block
-    # (measured), so with logits in the hundreds lse is only good to that
-    # relative precision; bf16 and fp32 keep the absolute 1e-3
+    # the e4m3 MFMA adds each run of 8 products aligned to the largest with
+    # about 14 bits (tests/test_fp8_accumulation_gpu.py), so with logits near
+    # 70 lse is only good to that relative precision; bf16 and fp32 keep the
+    # absolute 1e-3
     lse_tol = 1e-3 + (2.0 ** -13 * np.abs(lse_ref).max() if dtype == "fp8" else 0.0)
     compare(o, lse, o_ref, lse_ref, dtype, f"{dtype} scale={scale} causal={causal}", lse_tol=lse_tol)
+
+
+def _jump_inputs(N, d, seed):
+    """Q and K share a direction u: keys of the first half score about 0, keys of
+    the second half about 40 (58 in base-2 units), so every query that sees the
+    second half moves its reference max by more than the kernels' lazy-rescale
+    slack of 45 (base-2) and rescales its partial O by a factor in (0, 1)."""
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = 0.3 * rng.standard_normal((1, 2, N, d)) + 21.3 * u
+    k = 0.3 * rng.standard_normal((1, 2, N, d))
+    k[:, :, N // 2:] += 21.3 * u
+    v = rng.standard_normal((1, 2, N, d))
+    bf = lambda a: np.asarray(torch_bf16_round(a.astype(np.float32)), dtype=np.float32)
+    return bf(q), bf(k), bf(v)
+
+
+def torch_bf16_round(a):
+    import torch
+    return torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp8pv"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forced_rescale_d128(gpu_lib, dtype, causal):
+    """d = 128 (the LDS-DMA kernels of the headline, FP8 and FP8 P*V paths) with a
+    score jump that forces the O rescale; the jump is checked on the inputs."""
+    from parity_util import check_fp8pv, oracle_fp8pv
+    N, d = 1024, 128
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = _jump_inputs(N, d, 96)
+    s = scale * np.einsum("bhid,bhjd->bhij", q.astype(np.float64), k.astype(np.float64))
+    first, second = s[..., : N // 2].max(axis=-1), s[..., N // 2:].max(axis=-1)
+    assert np.all((second - first) * math.log2(math.e) > 45.0), "inputs do not force a rescale"
+    assert np.all(second < 60.0)
+    o, lse = gpu_forward(q, k, v, dtype, causal, scale)
+    if dtype == "fp8pv":
+        o_ref, lse_ref, a = oracle_fp8pv(q, k, v, causal, scale)
+        check_fp8pv(o, lse, o_ref, lse_ref, a, f"fp8pv rescale causal={causal}",
+                    lse_tol=1e-3 + 2.0 ** -13 * np.abs(lse_ref).max())
+        return
+    o_ref, lse_ref = oracle_forward(q, k, v, dtype, causal, scale)
+    lse_tol = 1e-3 + (2.0 ** -13 * np.abs(lse_ref).max() if dtype == "fp8" else 0.0)
+    compare(o, lse, o_ref, lse_ref, dtype, f"{dtype} rescale causal={causal}", lse_tol=lse_tol)
 
 
 def test_long_single_head_forward(gpu_lib):

@@ -22,7 +22,7 @@ import pytest
 
 import oracle
 from oracle.fp8 import decode_e4m3, quantize_tiles
-from parity_util import to_device
+from parity_util import check_fp8pv as _check, oracle_fp8pv as _oracle_fp8pv, to_device
 from tiled_attention_13_amd.inputs import WORKLOADS, Workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -50,29 +50,6 @@ def test_quant_v_bit_exact(gpu_lib, N, d):
     got = codes[:, :, :, pos[:N]].transpose(0, 1, 3, 2)    # back to [B, H, N, d]
     np.testing.assert_array_equal(got, ref_codes)
     assert np.all(codes[:, :, :, pos[N:]] == 0)
-
-
-def _oracle_fp8pv(q, k, v, causal, scale, rows=None):
-    q8, qs = quantize_tiles(q)
-    k8, ks = quantize_tiles(k)
-    v8, ve = oracle.quantize_v_pow2(v)
-    vd = oracle.dequantize_v_pow2(v8, ve)
-    qd, kd = decode_e4m3(q8), decode_e4m3(k8)
-    o, lse = oracle.attention_fp8(qd, qs, kd, ks, vd, causal, scale, rows=rows)
-    a, _ = oracle.attention_fp8(qd, qs, kd, ks, np.abs(vd), causal, scale, rows=rows)
-    return o, lse, a
-
-
-def _check(o, lse, o_ref, lse_ref, a, what):
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), what
-    err = np.abs(o - o_ref)
-    bound = 2.0 ** -4 * a + 2.0 ** -8 * np.abs(o_ref) + 5e-2
-    if np.any(err > bound):
-        i = np.unravel_index(np.argmax(err - bound), err.shape)
-        raise AssertionError(f"{what}: {int((err > bound).sum())} elements out of bound; worst {i}: gpu {o[i]:.5g} "
-                             f"ref {o_ref[i]:.5g} bound {bound[i]:.3g}")
-    assert np.abs(lse - lse_ref).max() <= 1e-3, what
-    return float(err.max())
 
 
 def _gpu(q, k, v, causal, scale):

@@ -89,6 +89,22 @@ def _check_qkv(q, k, v, torch_dtype):
             raise ValueError(f"{name} must be contiguous [B, H, N, d]")
         if t.dim() != 4 or t.shape != q.shape:
             raise ValueError("q, k, v must share one [B, H, N, d] shape")
+        if t.device != q.device:
+            raise ValueError("q, k, v must be on one device")
+
+
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output must be exactly what the kernels write: the
+    expected shape and dtype, contiguous, on the inputs' device (a smaller or
+    differently typed buffer would be written past its end)."""
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
 
 
 def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None, dtype: str | None = None,
@@ -111,8 +127,12 @@ def fwd(q, k, v, causal: bool = False, softmax_scale: float | None = None, dtype
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty_like(q)
+    else:
+        _check_out("out", out, q.shape, q.dtype, q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     st = load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                        int(bool(causal)), scale, code, _stream_ptr(stream))
     _check(st, "fa_fwd")
@@ -149,10 +169,16 @@ def fwd_fp8(q8, q_scale, k8, k_scale, v, causal: bool = False, softmax_scale: fl
     if q_scale.shape != (B, H, (N + 63) // 64) or k_scale.shape != q_scale.shape:
         raise ValueError("scales must be [B, H, ceil(N/64)]")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if q8.device != v.device or k8.device != v.device or q_scale.device != v.device or k_scale.device != v.device:
+        raise ValueError("q8, k8, scales and v must be on one device")
     if out is None:
         out = torch.empty_like(v)
+    else:
+        _check_out("out", out, v.shape, torch.bfloat16, v.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=v.device)
+    elif lse is not None:
+        _check_out("lse", lse, (B, H, N), torch.float32, v.device)
     st = load().fa_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), _ptr(v), _ptr(out), _ptr(lse),
                            B, H, N, d, int(bool(causal)), scale, _stream_ptr(stream))
     _check(st, "fa_fwd_fp8")
@@ -177,9 +203,17 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, softmax_scale: float | None
             or tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be the float32 [B, H, N] device tensor written by fwd")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("o", o), ("dout", dout), ("lse", lse)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    grads = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check_out(name, t, q.shape, torch.bfloat16, q.device)
+        grads.append(t)
+    dq, dk, dv = grads
     st = load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                        B, H, N, d, int(bool(causal)), scale, FA_BF16, _stream_ptr(stream))
     _check(st, "fa_bwd")
@@ -198,8 +232,14 @@ def fwd_partial(q, k, v, kv_begin: int, kv_end: int, causal: bool = False, softm
     _check_qkv(q, k, v, torch.bfloat16)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    o_part = torch.empty(q.shape, dtype=torch.float32, device=q.device) if o_part is None else o_part
-    lse_part = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse_part is None else lse_part
+    if o_part is None:
+        o_part = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    else:
+        _check_out("o_part", o_part, q.shape, torch.float32, q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    else:
+        _check_out("lse_part", lse_part, (B, H, N), torch.float32, q.device)
     st = load().fa_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(o_part), _ptr(lse_part), B, H, N, d,
                                int(kv_begin), int(kv_end), int(bool(causal)), scale, _stream_ptr(stream))
     _check(st, "fa_fwd_partial")
@@ -213,11 +253,15 @@ def merge(o_parts, lse_parts, out=None, lse=None, with_lse: bool = True, stream=
     if o_parts.dim() != 5 or o_parts.dtype != torch.float32 or not o_parts.is_contiguous() or not o_parts.is_cuda:
         raise ValueError("o_parts must be a contiguous float32 device tensor [G, B, H, N, d]")
     G, B, H, N, d = o_parts.shape
-    if lse_parts.dtype != torch.float32 or tuple(lse_parts.shape) != (G, B, H, N) or not lse_parts.is_contiguous():
-        raise ValueError("lse_parts must be a contiguous float32 device tensor [G, B, H, N]")
-    out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device) if out is None else out
+    _check_out("lse_parts", lse_parts, (G, B, H, N), torch.float32, o_parts.device)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=o_parts.device)
+    else:
+        _check_out("out", out, (B, H, N, d), torch.bfloat16, o_parts.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    elif lse is not None:
+        _check_out("lse", lse, (B, H, N), torch.float32, o_parts.device)
     st = load().fa_merge(_ptr(o_parts), _ptr(lse_parts), G, _ptr(out), _ptr(lse), B, H, N, d, _stream_ptr(stream))
     _check(st, "fa_merge")
     return out, lse
@@ -231,9 +275,14 @@ def fwd_splitkv(q, k, v, n_splits: int, causal: bool = False, softmax_scale: flo
     _check_qkv(q, k, v, torch.bfloat16)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out = torch.empty_like(q) if out is None else out
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_out("out", out, q.shape, torch.bfloat16, q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     st = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                int(bool(causal)), scale, int(n_splits), _stream_ptr(stream))
     _check(st, "fa_fwd_splitkv")
@@ -252,7 +301,7 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, softmax_scale: fl
     _check_qkv(q, k, v, torch.bfloat16)
     B, H, N, d = q.shape
     nb = (N + 63) // 64
-    if block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous():
+    if block_mask.dtype != torch.uint8 or block_mask.device != q.device or not block_mask.is_contiguous():
         raise ValueError("block_mask must be a contiguous uint8 device tensor")
     if tuple(block_mask.shape) == (nb, nb):
         stride = 0
@@ -261,9 +310,14 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, softmax_scale: fl
     else:
         raise ValueError(f"block_mask must be [{nb}, {nb}] or [{B}, {H}, {nb}, {nb}]")
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
-    out = torch.empty_like(q) if out is None else out
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_out("out", out, q.shape, torch.bfloat16, q.device)
     if lse is None and with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check_out("lse", lse, (B, H, N), torch.float32, q.device)
     st = load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, _ptr(block_mask),
                                    stride, int(bool(causal)), scale, _stream_ptr(stream))
     _check(st, "fa_fwd_blocksparse")

@@ -80,7 +80,10 @@ __device__ __forceinline__ void lds_barrier() {
 // buffer rsrc land at LDS byte lds + 16 * lane.  Issued through inline
 // assembly so that the compiler does not order every LDS read behind every
 // outstanding copy; the kernel waits for its own copies (vmcnt) before the
-// barrier that publishes a tile.
+// barrier that publishes a tile.  M0 is a reserved register for the compiler:
+// naming it in the clobber list is not honoured (clang warns that reserved
+// registers may not be preserved), so correctness rests on nothing else in
+// these kernels using M0, which the ISA test checks on every build.
 __device__ __forceinline__ void lds_dma16(uint32_t lds, u32x4 rsrc, uint32_t voff) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds), "v"(voff), "s"(rsrc)
                  : "memory");
