@@ -107,13 +107,13 @@ typedef enum {
  *   causal  : 0 or 1.
  *   softmax_scale : finite and > 0; multiplies the fp32 scores (it is not
  *             folded into the stored Q).
- *   dtype   : FA_F32, FA_BF16, FA_FP8_E4M3 or FA_FP8_E4M3_PV (workspace:
- *             e4m3 Q, K, V^T and their scales).  For FA_BF16 and
- *             FA_FP8_E4M3 the call allocates one stream-ordered workspace
- *             (hipMallocAsync / hipFreeAsync on `stream`) for V transposed
- *             (B*H*d*ceil(N/64)*64 bf16) and, for FA_FP8_E4M3, the quantised
- *             Q, K and their scales (it runs fa_quant_fp8_e4m3 on q and k
- *             before the FP8 kernel).  FA_F32 allocates nothing.
+ *   dtype   : FA_F32, FA_BF16, FA_FP8_E4M3 or FA_FP8_E4M3_PV.  FA_F32 and
+ *             FA_BF16 run one kernel and allocate nothing.  FA_FP8_E4M3
+ *             allocates one stream-ordered workspace (hipMallocAsync /
+ *             hipFreeAsync on `stream`) for the quantised Q, K and their
+ *             scales (it runs fa_quant_fp8_e4m3 on q and k before the FP8
+ *             kernel); FA_FP8_E4M3_PV also for the e4m3 V^T and its
+ *             exponents (fa_quant_v_pow2).
  * Returns FA_OK or the first error found.
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -155,8 +155,11 @@ fa_status fa_quant_v_pow2(const void* v_bf16, uint8_t* v8, uint8_t* v_scale, int
  *   q8, k8   : e4m3fn codes [B,H,N,d];  q_scale, k_scale : float32
  *              [B,H,ceil(N/64)] as written by fa_quant_fp8_e4m3.
  *   v_bf16   : bf16 [B,H,N,d];  o_bf16 : bf16 output [B,H,N,d];  lse as above.
- * Scores are softmax_scale * (q8 . k8) / (q_scale[i/64] * k_scale[j/64]),
- * the products taken on e4m3 matrix cores with fp32 accumulation.
+ * Scores are softmax_scale * (q8 . k8) / (q_scale[i/64] * k_scale[j/64])
+ * (Triton walkthrough page, section 4.1: the dequantisation multiplies the
+ * scores by 1/(q_scale * k_scale)), the products taken on e4m3 matrix cores,
+ * which add each run of 8 products aligned to the largest with about 14
+ * significant bits and accumulate those sums in fp32.  Allocates nothing.
  */
 fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8, const float* k_scale,
                      const void* v_bf16, void* o_bf16, float* lse,
@@ -178,7 +181,7 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
  *             the range (0 for a row that sees none of them).
  *   lse_part: float32 [B,H,N] output: ln of the range's softmax denominator
  *             (-inf for a row that sees none of its keys).
- * Allocates a stream-ordered V^T workspace like fa_fwd.
+ * Allocates nothing.
  */
 fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                          int64_t B, int64_t H, int64_t N, int64_t d, int64_t kv_begin, int64_t kv_end,
@@ -202,8 +205,8 @@ fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts
  * n_splits ranges of whole 64-key tiles that run as separate workgroups,
  * then merged as by fa_merge (1 <= n_splits <= 1024).  Same result as
  * fa_fwd up to rounding; it fills the device when B*H*ceil(N/256) is small.
- * Allocates one stream-ordered workspace: V^T plus n_splits float32 partial
- * O and lse (n_splits*B*H*N*(d+1)*4 bytes).
+ * Allocates one stream-ordered workspace: n_splits float32 partial O and
+ * lse (n_splits*B*H*N*(d+1)*4 bytes).
  */
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
@@ -222,7 +225,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
  *             table per (b, h)); anything else is FA_ERR_INVALID_ARGUMENT.
  * A row that sees no key gets O = 0 and lse = -inf.  Key tiles that no
  * query of a 256-row tile may see are never loaded.  Allocates one
- * stream-ordered workspace: V^T plus the per-tile visit lists
+ * stream-ordered workspace for the per-tile visit lists
  * (B*H*ceil(N/256)*(nb+1)*4 bytes).
  */
 fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,

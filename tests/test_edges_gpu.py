@@ -166,8 +166,9 @@ def test_repeated_runs_bit_identical(gpu_lib, path):
 
 def test_workspace_allocation_failure_is_reported(gpu_lib, monkeypatch):
     """With FA_TEST_FAIL_ALLOC=1 every entry point that needs a workspace returns
-    FA_ERR_OUT_OF_MEMORY (FAError status 9) and writes nothing; the fp32 forward,
-    which needs none, still runs; afterwards the same calls succeed."""
+    FA_ERR_OUT_OF_MEMORY (FAError status 9) and writes nothing; the fp32 and bf16
+    forwards and the FP8 forward on quantised inputs, which need none, still run
+    and write their outputs; afterwards the same calls succeed."""
     import torch
     import tiled_attention_13_amd as fa
     w = Workload("oom", 1, 2, 300, 128, "bf16", True, 95)
@@ -177,7 +178,6 @@ def test_workspace_allocation_failure_is_reported(gpu_lib, monkeypatch):
     tg = to_device(make_grad(w), "bf16")
     mask = torch.ones((5, 5), dtype=torch.uint8, device="cuda")
     calls = {
-        "bf16": lambda out: fa.fwd(tq, tk, tv, causal=True, out=out),
         "fp8": lambda out: fa.fwd(tq, tk, tv, causal=True, dtype="fp8", out=out),
         "fp8pv": lambda out: fa.fwd(tq, tk, tv, causal=True, dtype="fp8pv", out=out),
         "splitkv": lambda out: fa.fwd_splitkv(tq, tk, tv, 2, causal=True, out=out),
@@ -194,6 +194,14 @@ def test_workspace_allocation_failure_is_reported(gpu_lib, monkeypatch):
         assert torch.all(out == 7.0), name                    # nothing was enqueued
     q32, k32, v32 = (to_device(a, "f32") for a in (q, k, v))
     fa.fwd(q32, k32, v32, causal=True)                        # no workspace: unaffected
+    q8, qs = fa.quant_fp8(tq)
+    k8, ks = fa.quant_fp8(tk)
+    for name, call in (("bf16", lambda out: fa.fwd(tq, tk, tv, causal=True, out=out)),
+                       ("fp8 kernel", lambda out: fa.fwd_fp8(q8, qs, k8, ks, tv, causal=True, out=out))):
+        out = torch.full_like(tq, 7.0)
+        call(out)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all() and not torch.all(out == 7.0), name
     monkeypatch.delenv("FA_TEST_FAIL_ALLOC")
     for name, call in calls.items():
         call(torch.empty_like(tq))

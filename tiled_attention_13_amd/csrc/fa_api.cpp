@@ -68,16 +68,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int padded_keys(int n) { return (n + fa::kKeyTile - 1) / fa::kKeyTile * fa::kKeyTile; }
 
-// bytes of the V^T workspace of the bf16/FP8 kernel: [BH, d, N rounded up to a key tile] bf16
+// bytes of a transposed copy [BH, d, N rounded up to a key tile] bf16 (backward workspaces)
 size_t vt_bytes(int BH, int n, int d) { return static_cast<size_t>(BH) * d * padded_keys(n) * 2; }
-
-// The V^T workspace of the bf16/FP8 forward kernel: only head sizes that read V
-// transposed need it (the others transpose each tile in the kernel).
-size_t fwd_vt_bytes(int BH, int n, int d) { return fa::fwd_reads_vt(d) ? vt_bytes(BH, n, d) : 0; }
-
-hipError_t fwd_prepare_v(const void* v, void* vt, int BH, int n, int d, hipStream_t s) {
-    return fa::fwd_reads_vt(d) ? fa::launch_transpose_v(v, vt, BH, n, d, s) : hipSuccess;
-}
 
 // Stream-ordered workspace; a request of zero bytes allocates nothing.  With
 // FA_TEST_FAIL_ALLOC=1 in the environment (read at each call) every request
@@ -147,17 +139,9 @@ fa_status fa_fwd_fp8(const uint8_t* q8, const float* q_scale, const uint8_t* k8,
     if ((st = check_device()) != FA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
-    void* vt = nullptr;
-    if ((st = ws_alloc(&vt, fwd_vt_bytes(BH, n, dd), s)) != FA_OK) return st;
-    hipError_t e = fwd_prepare_v(v_bf16, vt, BH, n, dd, s);
-    if (e == hipSuccess) {
-        fa::FwdArgs a{fa::Kind::FP8, q8, k8, v_bf16, vt, o_bf16, lse, q_scale, k_scale,
-                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
-        e = fa::launch_fwd(a, s);
-    }
-    const hipError_t ef = ws_free(vt, s);
-    if (e != hipSuccess) return launch_status(e);
-    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+    fa::FwdArgs a{fa::Kind::FP8, q8, k8, v_bf16, nullptr, o_bf16, lse, q_scale, k_scale,
+                  BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+    return launch_status(fa::launch_fwd(a, s));
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
@@ -217,40 +201,34 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
         return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
     }
 
-    // bf16 / FP8: one stream-ordered workspace for V^T and, for FP8, the e4m3
-    // codes of Q and K and their per-tile scales
-    const bool fp8 = dtype == FA_FP8_E4M3;
+    if (dtype == FA_BF16) {
+        // one kernel, no workspace: V is read as it is
+        fa::FwdArgs a{fa::Kind::BF16, q, k, v, nullptr, o, lse, nullptr, nullptr, BH, n, padded_keys(n), dd,
+                      causal == 1, softmax_scale};
+        return launch_status(fa::launch_fwd(a, s));
+    }
+
+    // FP8: one stream-ordered workspace for the e4m3 codes of Q and K and their per-tile scales
     const size_t codes = static_cast<size_t>(BH) * n * dd;
     const size_t n_scales = static_cast<size_t>(BH) * ((n + 63) / 64);
-    const size_t off_vt = 0;
-    const size_t off_q8 = off_vt + round_up(fwd_vt_bytes(BH, n, dd), 256);
-    const size_t off_k8 = off_q8 + (fp8 ? round_up(codes, 256) : 0);
-    const size_t off_qs = off_k8 + (fp8 ? round_up(codes, 256) : 0);
-    const size_t off_ks = off_qs + (fp8 ? round_up(n_scales * 4, 256) : 0);
-    const size_t total = off_ks + (fp8 ? round_up(n_scales * 4, 256) : 0);
+    const size_t off_q8 = 0;
+    const size_t off_k8 = off_q8 + round_up(codes, 256);
+    const size_t off_qs = off_k8 + round_up(codes, 256);
+    const size_t off_ks = off_qs + round_up(n_scales * 4, 256);
+    const size_t total = off_ks + round_up(n_scales * 4, 256);
     void* ws = nullptr;
     if ((st = ws_alloc(&ws, total, s)) != FA_OK) return st;
     uint8_t* base = static_cast<uint8_t*>(ws);
-    void* vt = base + off_vt;
-    hipError_t e = fwd_prepare_v(v, vt, BH, n, dd, s);
-    if (!fp8) {
-        if (e == hipSuccess) {
-            fa::FwdArgs a{fa::Kind::BF16, q, k, v, vt, o, lse, nullptr, nullptr, BH, n, padded_keys(n), dd,
-                          causal == 1, softmax_scale};
-            e = fa::launch_fwd(a, s);
-        }
-    } else {
-        uint8_t* q8 = base + off_q8;
-        uint8_t* k8 = base + off_k8;
-        float* qs = reinterpret_cast<float*>(base + off_qs);
-        float* ks = reinterpret_cast<float*>(base + off_ks);
-        if (e == hipSuccess) e = fa::launch_quant_fp8(q, q8, qs, BH, n, dd, s);
-        if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, ks, BH, n, dd, s);
-        if (e == hipSuccess) {
-            fa::FwdArgs a{fa::Kind::FP8, q8, k8, v, vt, o, lse, qs, ks, BH, n, padded_keys(n), dd, causal == 1,
-                          softmax_scale};
-            e = fa::launch_fwd(a, s);
-        }
+    uint8_t* q8 = base + off_q8;
+    uint8_t* k8 = base + off_k8;
+    float* qs = reinterpret_cast<float*>(base + off_qs);
+    float* ks = reinterpret_cast<float*>(base + off_ks);
+    hipError_t e = fa::launch_quant_fp8(q, q8, qs, BH, n, dd, s);
+    if (e == hipSuccess) e = fa::launch_quant_fp8(k, k8, ks, BH, n, dd, s);
+    if (e == hipSuccess) {
+        fa::FwdArgs a{fa::Kind::FP8, q8, k8, v, nullptr, o, lse, qs, ks, BH, n, padded_keys(n), dd, causal == 1,
+                      softmax_scale};
+        e = fa::launch_fwd(a, s);
     }
     const hipError_t ef = ws_free(ws, s);
     if (e != hipSuccess) return launch_status(e);
@@ -276,23 +254,15 @@ fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_p
     if ((st = check_device()) != FA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
-    void* vt = nullptr;
-    if ((st = ws_alloc(&vt, fwd_vt_bytes(BH, n, dd), s)) != FA_OK) return st;
-    hipError_t e = fwd_prepare_v(v, vt, BH, n, dd, s);
-    if (e == hipSuccess) {
-        fa::FwdArgs a{fa::Kind::BF16, q, k, v, vt, nullptr, nullptr, nullptr, nullptr,
-                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
-        a.o32 = o_part;
-        a.lse_part = lse_part;
-        a.kt_lo = static_cast<int>(kv_begin / fa::kKeyTile);
-        a.kt_hi = static_cast<int>((kv_end + fa::kKeyTile - 1) / fa::kKeyTile);
-        a.tps = a.kt_hi > a.kt_lo ? a.kt_hi - a.kt_lo : 1;
-        a.n_splits = 1;
-        e = fa::launch_fwd(a, s);
-    }
-    const hipError_t ef = ws_free(vt, s);
-    if (e != hipSuccess) return launch_status(e);
-    return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+    fa::FwdArgs a{fa::Kind::BF16, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+    a.o32 = o_part;
+    a.lse_part = lse_part;
+    a.kt_lo = static_cast<int>(kv_begin / fa::kKeyTile);
+    a.kt_hi = static_cast<int>((kv_end + fa::kKeyTile - 1) / fa::kKeyTile);
+    a.tps = a.kt_hi > a.kt_lo ? a.kt_hi - a.kt_lo : 1;
+    a.n_splits = 1;
+    return launch_status(fa::launch_fwd(a, s));
 }
 
 fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse,
@@ -328,7 +298,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
     const int n_tiles = (n + fa::kKeyTile - 1) / fa::kKeyTile;
     const int tps = (n_tiles + static_cast<int>(n_splits) - 1) / static_cast<int>(n_splits);
     const size_t rows = static_cast<size_t>(BH) * n;
-    const size_t off_o32 = round_up(fwd_vt_bytes(BH, n, dd), 256);
+    const size_t off_o32 = 0;
     const size_t off_lse = off_o32 + round_up(static_cast<size_t>(n_splits) * rows * dd * 4, 256);
     const size_t total = off_lse + round_up(static_cast<size_t>(n_splits) * rows * 4, 256);
     void* ws = nullptr;
@@ -336,9 +306,9 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
     uint8_t* base = static_cast<uint8_t*>(ws);
     float* o32 = reinterpret_cast<float*>(base + off_o32);
     float* lse_part = reinterpret_cast<float*>(base + off_lse);
-    hipError_t e = fwd_prepare_v(v, base, BH, n, dd, s);
-    if (e == hipSuccess) {
-        fa::FwdArgs a{fa::Kind::BF16, q, k, v, base, nullptr, nullptr, nullptr, nullptr,
+    hipError_t e = hipSuccess;
+    {
+        fa::FwdArgs a{fa::Kind::BF16, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr,
                       BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
         a.o32 = o32;
         a.lse_part = lse_part;
@@ -371,7 +341,7 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
     const size_t n_lists = static_cast<size_t>(BH) * ((n + fa::kQueryTile - 1) / fa::kQueryTile);
-    const size_t off_list = round_up(fwd_vt_bytes(BH, n, dd), 256);
+    const size_t off_list = 0;
     const size_t off_cnt = off_list + round_up(n_lists * static_cast<size_t>(nb) * 4, 256);
     const size_t total = off_cnt + round_up(n_lists * 4, 256);
     void* ws = nullptr;
@@ -379,10 +349,9 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
     uint8_t* base = static_cast<uint8_t*>(ws);
     uint32_t* list = reinterpret_cast<uint32_t*>(base + off_list);
     int* cnt = reinterpret_cast<int*>(base + off_cnt);
-    hipError_t e = fwd_prepare_v(v, base, BH, n, dd, s);
-    if (e == hipSuccess) e = fa::launch_bs_plan(block_mask, mask_bh_stride, BH, n, causal == 1, list, cnt, s);
+    hipError_t e = fa::launch_bs_plan(block_mask, mask_bh_stride, BH, n, causal == 1, list, cnt, s);
     if (e == hipSuccess) {
-        fa::FwdArgs a{fa::Kind::BF16, q, k, v, base, o, lse, nullptr, nullptr,
+        fa::FwdArgs a{fa::Kind::BF16, q, k, v, nullptr, o, lse, nullptr, nullptr,
                       BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
         a.bs_list = list;
         a.bs_count = cnt;

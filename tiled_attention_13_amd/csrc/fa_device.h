@@ -53,20 +53,33 @@ __device__ __forceinline__ int vt_slot(int kk) {
     return 16 * c + 8 * hh + 4 * a + b;
 }
 
-// Scheduling pattern for a block of N (16-byte LDS read -> MFMA) pairs: issue
-// AHEAD reads first, then alternate one MFMA with one further read, so each
-// MFMA's operand was requested about AHEAD MFMAs (~32 cycles each) earlier.
+// Scheduling pattern for N MFMAs whose operands come from R LDS reads each:
+// issue the reads of the first AHEAD MFMAs, then alternate one MFMA with the
+// reads of a further one, so each MFMA's operand was requested about AHEAD
+// MFMAs (~32 cycles each) earlier.
 constexpr int kLdsAhead = 6;
-template <int N, int AHEAD>
+template <int N, int AHEAD, int R = 1>
 __device__ __forceinline__ void pipeline_lds_mfma() {
     constexpr int A = AHEAD < N ? AHEAD : N;
-    __builtin_amdgcn_sched_group_barrier(0x100, A, 0);          // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x100, A * R, 0);      // DS reads
 #pragma unroll
     for (int i = 0; i < N - A; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);      // DS reads
     }
     __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lanes 4r .. 4r+3 each name 8 bytes (four 16-bit values) that together
+// form row r of a 4 x 16 matrix; lane i of the group receives column i, i.e.
+// value i of rows 0, 1, 2, 3.  (Measured on the device with an in-bounds probe.)
+__device__ __forceinline__ i16x4 ds_read_tr16(const lds_u8* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<lds_u8*>(p)));
 }
 
 // Barrier that orders LDS traffic only: outstanding global loads stay in flight.

@@ -13,8 +13,10 @@
 // scores of ONE query (the other 16 of each 32-key block sit in lane l ^ 32).
 // Row reductions are in-lane plus one v_permlane32_swap, and the
 // probabilities already sit where the B operand of O^T += V^T P^T wants
-// them: P never goes through LDS.  V^T comes from a pre-pass that
-// transposes V once per call (keys permuted within each tile to match).
+// them: P never goes through LDS.  V tiles sit in LDS as they are in memory
+// (key rows, 16-byte granules XOR-swizzled per row) and the V^T operand of
+// that product is gathered with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16), so no transposed copy of V is ever made.
 //
 // Online softmax (Triton walkthrough page, section 2.1): running max m and
 // running sum l per query, kept in base-2 units with softmax_scale*log2(e)
@@ -149,6 +151,18 @@ __device__ __forceinline__ float softmax_step_p8(float (&s)[NS], float c, float&
     return alpha;
 }
 
+// 16-byte granule of a bf16 V key row in LDS: data granule g of key row `row`
+// sits at granule v_granule<D>(row, g), an XOR and so its own inverse.  The
+// transposing reads of the P*V operand take, per 32 lanes, four consecutive
+// key rows x 64 bytes (32 head dims); the swizzle puts those four pieces on
+// four distinct quarters of the 64 LDS banks.
+template <int D>
+__device__ __forceinline__ int v_granule(int row, int g) {
+    if constexpr (D == 128) return g ^ (4 * (row & 3));
+    else if constexpr (D == 64) return g ^ (4 * ((row >> 1) & 1));
+    else return g;
+}
+
 // Byte position, inside a 64-key row of the e4m3 V^T, of key kk: the order in
 // which one lane's 32 P values (the two 32-key score blocks of its query, in
 // register order) meet the k-slots of the 32x32x64 e4m3 MFMA.
@@ -192,30 +206,29 @@ struct PPCfg {
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
     static constexpr int VES = PV8 ? 1 : 2;      // bytes per V element
-    static constexpr int VROW = VES * BN + 16;   // bytes per V^T row in LDS (padded)
+    // bf16 V: BN key rows of D*2 bytes, granules swizzled (v_granule); e4m3 V
+    // (FP8 P*V): D rows of V^T, BN keys each plus 16 bytes of padding
+    static constexpr int VROW = PV8 ? VES * BN + 16 : D * 2;
     static constexpr int KBYTES = BN * KROW;
-    static constexpr int VBYTES = D * VROW;
+    static constexpr int VBYTES = PV8 ? D * VROW : BN * VROW;
     static constexpr int SBYTES = PV8 ? (D + 15) / 16 * 16 : 0;   // V block exponents of the tile
     static constexpr int STAGE = KBYTES + VBYTES + SBYTES;
     static constexpr int K_CPR = D * ES / 16;    // 16-byte chunks per K row
     static constexpr int K_CHUNKS = BN * K_CPR;
     static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-    // small heads read V [N, d] rows and transpose each tile into LDS; the
-    // others copy rows of the V^T workspace
-    static constexpr bool VNAT = !PV8 && D < kVtMinD;
-    static constexpr int V_CPR = VNAT ? D * 2 / 16 : VES * BN / 16;   // 16-byte chunks per V (V^T) row
-    static constexpr int V_CHUNKS = VNAT ? BN * V_CPR : D * V_CPR;    // 16-byte chunks of a V tile
+    static constexpr int V_CPR = PV8 ? BN / 16 : D * 2 / 16;       // 16-byte chunks per V (e4m3 V^T) row
+    static constexpr int V_CHUNKS = PV8 ? D * V_CPR : BN * V_CPR;    // 16-byte chunks of a V tile
     static constexpr int V_PER_T = (V_CHUNKS + NT - 1) / NT;
     static constexpr bool F8W = FP8 && (D % 64 == 0);
     static constexpr bool F8N = FP8 && !F8W;
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
 
-// Dense kernels for heads below 128 ask for 128 VGPRs (four waves per SIMD: two
-// workgroups per CU); the partial-result and block-sparse modes keep the wider
-// budget, which they need.
+// The dense d = 32 kernels ask for 128 VGPRs (four waves per SIMD: two
+// workgroups per CU); the others keep the wider budget, which they need (at
+// d = 64 the transposing V reads take the dense kernel past 128).
 template <int D, bool CAUSAL, bool FP8, int MODE, bool PV8 = false>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((D < 128 && MODE == kModeDense) ? 4 : 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((D == 32 && MODE == kModeDense) ? 4 : 2)))
 void fwd_pp_kernel(KParams p) {
     using C = PPCfg<D, CAUSAL, FP8, PV8, MODE>;
     constexpr bool PARTIAL = MODE == kModePartial, SPARSE = MODE == kModeSparse;
@@ -243,8 +256,8 @@ void fwd_pp_kernel(KParams p) {
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* qg = p.q + slice * ES;
     const uint8_t* kg = p.k + slice * ES;
-    // V^T rows of this (b, h): D rows of np keys
-    const uint8_t* vtg = C::VNAT ? p.v + slice * 2 : p.vt + static_cast<size_t>(bh) * D * p.np * C::VES;
+    // V of this (b, h): [N, D] bf16 rows, or (FP8 P*V) the e4m3 V^T, D rows of np keys
+    const uint8_t* vg = PV8 ? p.vt + static_cast<size_t>(bh) * D * p.np : p.v + slice * 2;
 
     // ---- Q fragments (B operand of S^T = K Q^T)
     u32x4 qf[C::F8W ? 2 * C::QREGS : C::QREGS];
@@ -328,12 +341,14 @@ void fwd_pp_kernel(KParams p) {
     // is fixed, and rows past the end of the sequence read as zero (the hardware
     // range check), so full and partial tiles share one path.
     // DMA path: a stage is BN K rows (KROW-byte stride: D*ES/16 granules of 16
-    // bytes + one pad granule) then D V^T rows (VROW: BN*VES/16 + 1 granules),
+    // bytes + one pad granule) then the V tile (BN key rows of D*2 bytes with
+    // swizzled granules; FP8 P*V: D e4m3 V^T rows, BN/16 granules + one pad),
     // i.e. DMA_ALL contiguous 1 KiB blocks, one LDS-DMA instruction each; group
     // A copies the first DMA_A blocks, group B the rest, block b of a group by
-    // its wave b mod 4.  A lane that falls on a pad granule reads past the
-    // buffer (zero, no memory traffic).  The FP8 P*V block exponents after them
-    // still go through registers.
+    // its wave b mod 4.  Each lane's source offset is chosen so that its 16
+    // bytes land where the layout wants them; a lane that falls on a pad
+    // granule reads past the buffer (zero, no memory traffic).  The FP8 P*V
+    // block exponents after them still go through registers.
     constexpr int DMA_K = C::KBYTES / 1024, DMA_ALL = (C::KBYTES + C::VBYTES) / 1024;
     constexpr int DMA_A = (DMA_ALL + 1) / 2, DMA_PER_W = (DMA_A + 3) / 4;
     constexpr int KG = C::KROW / 16, KD = D * ES / 16, VG = C::VROW / 16, VD = BN * C::VES / 16;
@@ -341,7 +356,7 @@ void fwd_pp_kernel(KParams p) {
     int dma_n = 0;
     uint32_t smem_lds = 0;
     if constexpr (C::DMA) {
-        static_assert(C::KBYTES % 1024 == 0 && C::VBYTES % 1024 == 0 && KG == KD + 1 && VG == VD + 1,
+        static_assert(C::KBYTES % 1024 == 0 && C::VBYTES % 1024 == 0 && KG == KD + 1 && (!PV8 || VG == VD + 1),
                       "LDS-DMA layout");
         smem_lds = static_cast<uint32_t>(reinterpret_cast<size_t>((__attribute__((address_space(3))) uint8_t*)smem));
         const int b0 = grp == 0 ? 0 : DMA_A, b1 = grp == 0 ? DMA_A : DMA_ALL;
@@ -353,9 +368,13 @@ void fwd_pp_kernel(KParams p) {
                 if (b < DMA_K) {
                     const int g = 64 * b + lane, row = g / KG, col = g - KG * row;
                     if (col < KD) off = row * (D * ES) + 16 * col;
-                } else {
+                } else if constexpr (PV8) {
                     const int g = 64 * (b - DMA_K) + lane, row = g / VG, col = g - VG * row;
-                    if (col < VD) off = static_cast<uint32_t>(row) * p.np * C::VES + 16 * col;
+                    if (col < VD) off = static_cast<uint32_t>(row) * p.np + 16 * col;
+                } else {
+                    // LDS granule pos of key row `row` holds V granule v_granule<D>(row, pos)
+                    const int g = 64 * (b - DMA_K) + lane, row = g / VG, pos = g - VG * row;
+                    off = row * (D * 2) + 16 * v_granule<D>(row, pos);
                 }
                 dma_n = i + 1;
             }
@@ -365,11 +384,12 @@ void fwd_pp_kernel(KParams p) {
     auto dma_tile = [&](int t) {
         const int n0 = tile_of(t) * BN;
         const uint64_t ka = reinterpret_cast<uint64_t>(kg + static_cast<size_t>(n0) * D * ES);
-        const uint64_t va = reinterpret_cast<uint64_t>(vtg + static_cast<size_t>(n0) * C::VES);
+        const uint64_t va = reinterpret_cast<uint64_t>(PV8 ? vg + n0 : vg + static_cast<size_t>(n0) * D * 2);
         const u32x4 kr = {static_cast<uint32_t>(ka), static_cast<uint32_t>(ka >> 32) & 0xFFFFu,
                           static_cast<uint32_t>(min(N - n0, BN) * D * ES), static_cast<uint32_t>(kBufferFlags)};
         const u32x4 vr = {static_cast<uint32_t>(va), static_cast<uint32_t>(va >> 32) & 0xFFFFu,
-                          (static_cast<uint32_t>(D) * p.np - n0) * C::VES, static_cast<uint32_t>(kBufferFlags)};
+                          PV8 ? static_cast<uint32_t>(D) * p.np - n0 : static_cast<uint32_t>(min(N - n0, BN) * D * 2),
+                          static_cast<uint32_t>(kBufferFlags)};
         const uint32_t stage = smem_lds + (t % C::STAGES) * C::STAGE;
         const int b0 = (grp == 0 ? 0 : DMA_A) + (w & 3);
 #pragma unroll
@@ -394,12 +414,11 @@ void fwd_pp_kernel(KParams p) {
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(kg + static_cast<size_t>(n0) * D * ES), 0,
             static_cast<int>(static_cast<uint32_t>(min(N - n0, BN) * D * ES)), kBufferFlags);
-        const __amdgpu_buffer_rsrc_t vr = C::VNAT
-            ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vtg + static_cast<size_t>(n0) * D * 2), 0,
+        const __amdgpu_buffer_rsrc_t vr = PV8
+            ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vg + n0), 0,
+                                                static_cast<int>(static_cast<uint32_t>(D) * p.np - n0), kBufferFlags)
+            : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vg + static_cast<size_t>(n0) * D * 2), 0,
                                                 static_cast<int>(static_cast<uint32_t>(min(N - n0, BN) * D * 2)),
-                                                kBufferFlags)
-            : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(vtg + static_cast<size_t>(n0) * C::VES), 0,
-                                                static_cast<int>((static_cast<uint32_t>(D) * p.np - n0) * C::VES),
                                                 kBufferFlags);
         if constexpr (PV8) {
             if (tid < C::SBYTES / 16)
@@ -417,10 +436,10 @@ void fwd_pp_kernel(KParams p) {
         for (int i = 0; i < C::V_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
-                const int d = c / C::V_CPR, col = c - d * C::V_CPR;   // (VNAT: d is the key)
+                const int row = c / C::V_CPR, col = c - row * C::V_CPR;   // key row (FP8 P*V: V^T row)
                 vst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    vr, C::VNAT ? d * D * 2 + 16 * col
-                                : static_cast<int>(static_cast<uint32_t>(d) * p.np * C::VES + 16 * col), 0, 0);
+                    vr, PV8 ? static_cast<int>(static_cast<uint32_t>(row) * p.np + 16 * col) : row * D * 2 + 16 * col,
+                    0, 0);
             }
         }
     };
@@ -447,20 +466,11 @@ void fwd_pp_kernel(KParams p) {
         for (int i = 0; i < C::V_PER_T; ++i) {
             const int c = i * NT + tid;
             if (c < C::V_CHUNKS) {
-                const int d = c / C::V_CPR, col = c - d * C::V_CPR;
-                if constexpr (C::VNAT) {
-                    // key d, dims 8 col .. 8 col + 7: one bf16 into each V^T row, at the
-                    // key's slot (vt_slot is its own inverse)
-                    uint8_t* dst = vs + 8 * col * C::VROW + 2 * vt_slot(d);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        *reinterpret_cast<uint16_t*>(dst + 2 * e * C::VROW) = static_cast<uint16_t>(vst[i][e]);
-                        *reinterpret_cast<uint16_t*>(dst + (2 * e + 1) * C::VROW) =
-                            static_cast<uint16_t>(vst[i][e] >> 16);
-                    }
-                } else {
-                    *reinterpret_cast<u32x4*>(vs + d * C::VROW + 16 * col) = vst[i];
-                }
+                const int row = c / C::V_CPR, col = c - row * C::V_CPR;
+                // v_granule is an involution in the granule index: data granule col
+                // goes to LDS granule v_granule(row, col)
+                const int pos = PV8 ? col : v_granule<D>(row, col);
+                *reinterpret_cast<u32x4*>(vs + row * C::VROW + 16 * pos) = vst[i];
             }
         }
         if constexpr (PV8) {
@@ -479,9 +489,25 @@ void fwd_pp_kernel(KParams p) {
     uint32_t pf8[BN / 8];                        // FP8 P*V: the lane's 32 P values as e4m3 codes
     int p_scale = 127;                           // FP8 P*V: block exponent of those codes
 
-    // per-lane LDS addresses of this lane's K row / V^T row fragments in stage 0
+    // per-lane LDS addresses of this lane's K row / e4m3 V^T row fragments in stage 0
     const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
-    const uint8_t* lane_v = smem + C::KBYTES + l32 * C::VROW + (PV8 ? 32 : 16) * h;
+    const uint8_t* lane_v = smem + C::KBYTES + l32 * C::VROW + 32 * h;
+    // bf16 V: A operand of O^T += V^T P^T for 32 head dims (db) and 16 keys
+    // (chunk cc).  The MFMA's k index 8h + t meets key 16cc + 4h + 8(t >> 2) +
+    // (t & 3) in the probability fragment (the S^T accumulator layout), so lane
+    // (dim 32db + l32, half h) needs V[16cc + 4h + {0..3}][dim] and
+    // V[16cc + 8 + 4h + {0..3}][dim]: two transposing reads, in which lane
+    // 16g + 4r + j names dims 32db + 16(g & 1) + 4j .. +3 of key row
+    // 16cc + 4(g >> 1) + r (+ 8).  Byte offset of the first read of chunk 0,
+    // within a stage's V tile, per db:
+    uint32_t lane_vo[D / 32];
+    {
+        const int g = lane >> 4, r = (lane >> 2) & 3, j = lane & 3;
+        const int t = D == 128 ? r : (D == 64 ? (r >> 1) & 1 : 0);    // the row's swizzle, in granule quads
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            lane_vo[db] = (4 * (g >> 1) + r) * C::VROW + 64 * (db ^ t) + 16 * (2 * (g & 1) + (j >> 1)) + 8 * (j & 1);
+    }
 
     // ---- the four ops of the schedule
     // S^T = K_j Q^T for tile j
@@ -546,8 +572,8 @@ void fwd_pp_kernel(KParams p) {
     };
     // O^T += V_j^T P^T for tile j
     auto op_pv = [&](int j) {
-        const uint8_t* vl = lane_v + (j % C::STAGES) * C::STAGE;
         if constexpr (PV8) {
+            const uint8_t* vl = lane_v + (j % C::STAGES) * C::STAGE;
             // O^T += V^T P^T on the 32x32x64 e4m3 MFMA: one per 32 rows of d covers the
             // whole 64-key tile; both operands carry their power-of-two block exponents
             const uint8_t* sc = smem + (j % C::STAGES) * C::STAGE + C::KBYTES + C::VBYTES;
@@ -566,17 +592,23 @@ void fwd_pp_kernel(KParams p) {
         }
         constexpr int NA = (D / 32) * (BN / 16);
         bf16x8 a[NA];
+        const lds_u8* vs = (const lds_u8*)smem + (j % C::STAGES) * C::STAGE + C::KBYTES;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db) {
+            const lds_u8* vb = vs + lane_vo[db];
 #pragma unroll
-            for (int cc = 0; cc < BN / 16; ++cc)
-                a[db * (BN / 16) + cc] = __builtin_bit_cast(bf16x8, ld16(vl + 32 * db * C::VROW + 32 * cc));
+            for (int cc = 0; cc < BN / 16; ++cc) {
+                const i16x4 lo = ds_read_tr16(vb + 16 * cc * C::VROW);
+                const i16x4 hi = ds_read_tr16(vb + (16 * cc + 8) * C::VROW);
+                a[db * (BN / 16) + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int cc = 0; cc < BN / 16; ++cc)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db * (BN / 16) + cc], pf[cc], o[db], 0, 0, 0);
-        pipeline_lds_mfma<NA, kLdsAhead>();
+        pipeline_lds_mfma<NA, kLdsAhead, 2>();
     };
     // softmax of tile j, rescale of O, probabilities packed to bf16
     auto op_softmax = [&](int j, bool masked) {

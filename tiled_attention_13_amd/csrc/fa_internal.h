@@ -13,15 +13,14 @@ struct FwdArgs {
     const void* q;          // f32 / bf16 / e4m3 codes
     const void* k;
     const void* v;          // f32 or bf16
-    const void* vt;         // bf16/FP8 kernels: V transposed by launch_transpose_v, [BH, d, np];
-                            // FP8PV: e4m3 V^T from launch_quant_v_pow2, [BH, d, np] bytes
+    const void* vt;         // FP8PV only: e4m3 V^T from launch_quant_v_pow2, [BH, d, np] bytes
     void* o;                // f32 or bf16
     float* lse;             // may be null
     const float* q_scale;   // FP8 only: [BH, ceil(N/64)]
     const float* k_scale;
     int BH;
     int N;
-    int np;                 // row length of vt: N rounded up to the 64-key tile
+    int np;                 // row length of vt (FP8PV): N rounded up to the 64-key tile
     int d;
     bool causal;
     float softmax_scale;
@@ -58,22 +57,16 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 // Keys per tile of the bf16/FP8 attention kernel; V^T rows are padded to a multiple of it.
 constexpr int kKeyTile = 64;
 
-// Head sizes from which the bf16/FP8 attention kernel reads V through the V^T
-// workspace of launch_transpose_v; below it the kernel reads V [BH, N, d] as it
-// is and transposes each tile on its way into LDS (the FP8 P*V kernel always
-// reads the e4m3 V^T of launch_quant_v_pow2).
-constexpr int kVtMinD = 128;
-inline bool fwd_reads_vt(int d) { return d >= kVtMinD; }
-
 // Enqueue the merge of n_parts partial results (o_parts [n_parts, BH, N, d]
 // fp32, lse_parts [n_parts, BH, N]) into bf16 o [BH, N, d] and lse (may be null):
 // lse = ln sum_g exp(lse_g), O = sum_g exp(lse_g - lse) O_g.
 hipError_t launch_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
                         int BH, int N, int d, hipStream_t stream);
 
-// Enqueue the transposition of a bf16 V [BH, N, d] into vt [BH, d, np] (np = N rounded
-// up to kKeyTile, padding zero), keys permuted within each tile into the order the
-// attention kernel's LDS layout uses.  vt must hold BH * d * np bf16 values.
+// Enqueue the transposition of a bf16 [BH, N, d] tensor into [BH, d, np] (np = N
+// rounded up to kKeyTile, padding zero), keys permuted within each tile into the
+// order the backward kernels' LDS layouts use.  The output must hold BH * d * np
+// bf16 values.
 hipError_t launch_transpose_v(const void* v, void* vt, int BH, int N, int d, hipStream_t stream);
 
 struct BwdArgs {
