@@ -29,18 +29,30 @@ with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
 matrix-core FLOPs the kernels actually execute (4 x: the dV, dK and dQ
 kernels each recompute S, and dK and dQ both compute dP).
 
-``--calib-copy-mib`` runs, after the timed loop, a plain device copy of M MiB
-so that a counter run (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE) sees a kernel
-of known traffic next to the attention kernel.
+Hardware counters: before it touches the GPU, the script runs itself three
+times under ``rocprofv3 --pmc`` (one counter pass each, two timed calls after
+one warm-up, then a 1 GiB device copy of known traffic) and reports, for the
+attention kernel, MFMA busy, the LDS bank-conflict share, the shader clock and
+the HBM bytes read and written (FETCH_SIZE / WRITE_SIZE scaled by what the
+same counters read for the copy).  ``--no-counters`` skips them;
+``--counter-dir D`` keeps the raw rocprofv3 output; ``--write-profile F``
+writes the counter summary with the hash of the kernel sources it was taken
+on.  ``--calib-copy-mib`` runs, after the timed loop, a plain device copy of
+M MiB (what the counter passes use).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
 import platform
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -54,7 +66,16 @@ PEAK_HBM_GBPS = 8000.0
 # the forward kernel's code: the HBM traffic summary is valid while these are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_13_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_bf16_traffic.json")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_bf16_counters.json")
+# rocprofv3 counter passes (each within one run's hardware limits: at most 8 SQ,
+# 2 GRBM and 4 TCC counters; FETCH_SIZE takes 3 TCC counters, WRITE_SIZE 2)
+COUNTER_PASSES = (
+    ("core", ("GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE")),
+    ("fetch", ("FETCH_SIZE",)),
+    ("write", ("WRITE_SIZE",)),
+)
+CALIB_MIB = 1024
+N_XCD, N_SIMD_TOTAL = 8, 1024
 
 
 def kernel_source_hash() -> str:
@@ -65,16 +86,114 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it was taken on this kernel source."""
+def committed_counters(workload: str):
+    """The committed counter summary, if it was taken on this kernel source and workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(COUNTER_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload") != workload:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def _rocprofv3():
+    for cand in (shutil.which("rocprofv3"), "/opt/rocm/bin/rocprofv3"):
+        if cand and os.path.exists(cand):
+            return cand
+    return None
+
+
+def _counter_rows(d: str):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_kernel(rows, counter: str, match: str):
+    """Per-dispatch values of one counter for the kernels whose name contains `match`."""
+    by = {}
+    for r in rows:
+        if r.get("Counter_Name") == counter and match in r.get("Kernel_Name", ""):
+            by[r["Dispatch_Id"]] = (float(r["Counter_Value"]), int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                                    r["Kernel_Name"])
+    return [by[k] for k in sorted(by, key=int)]
+
+
+def kernel_match(w) -> str:
+    """Substring of the attention kernel's name in rocprofv3 output for a workload."""
+    if w.dtype == "f32":
+        return "fwd_f32_kernel"
+    return f"fwd_pp_kernel<{w.d}, {'true' if w.causal else 'false'}, {'true' if w.dtype != 'bf16' else 'false'}, 0"
+
+
+def collect_counters(w, keep_dir=None, timeout_s: float = 150.0) -> dict:
+    """Counter passes in child processes (rocprofv3 --pmc ... -- python3 bench.py --counter-child ...).
+
+    Must run before this process touches the GPU.  Returns the derived figures
+    for the attention kernel, or {"error": ...}."""
+    rp = _rocprofv3()
+    if rp is None:
+        return {"error": "rocprofv3 not found"}
+    base = keep_dir or tempfile.mkdtemp(prefix="fa_pmc_")
+    child = [sys.executable, os.path.abspath(__file__), "--counter-child", "--workload", w.name,
+             "--steps", "2", "--warmup", "1", "--calib-copy-mib", str(CALIB_MIB)]
+    rows, cmds = {}, []
+    try:
+        for name, ctrs in COUNTER_PASSES:
+            d = os.path.join(base, f"pmc_{name}")
+            cmd = [rp, "--pmc", *ctrs, "--output-format", "csv", "-d", d, "-o", "p", "--", *child]
+            cmds.append(" ".join(["rocprofv3", "--pmc", *ctrs, "--output-format", "csv", "-d", f"<dir>/pmc_{name}",
+                                  "-o", "p", "--", "python3", "bench.py", *child[2:]]))
+            print(f"[bench] counter pass {name}: {' '.join(ctrs)}", file=sys.stderr, flush=True)
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout_s, cwd=ROOT)
+            rows[name] = _counter_rows(d)
+            if not rows[name]:
+                return {"error": f"pass {name}: rocprofv3 exited {r.returncode} with no counter rows; "
+                                 f"stderr tail: {r.stderr[-400:]}"}
+    except subprocess.TimeoutExpired:
+        return {"error": f"a counter pass exceeded {timeout_s} s"}
+    finally:
+        if keep_dir is None:
+            shutil.rmtree(base, ignore_errors=True)
+    return {**derive_counters(rows, kernel_match(w)), "commands": cmds}
+
+
+def derive_counters(rows: dict, m: str) -> dict:
+    """Figures for the kernels whose name contains `m` from the rows of the three passes."""
+    get = lambda p, c, k=m: _per_kernel(rows[p], c, k)
+    gui, mfma = get("core", "GRBM_GUI_ACTIVE"), get("core", "SQ_VALU_MFMA_BUSY_CYCLES")
+    bank, lds = get("core", "SQ_LDS_BANK_CONFLICT"), get("core", "SQ_LDS_IDX_ACTIVE")
+    fetch, write = get("fetch", "FETCH_SIZE"), get("write", "WRITE_SIZE")
+    cf, cw = get("fetch", "FETCH_SIZE", "copyBuffer"), get("write", "WRITE_SIZE", "copyBuffer")
+    if not (gui and mfma and bank and lds and fetch and write and cf and cw):
+        return {"error": f"counter rows missing for '{m}' or the calibration copy"}
+    mean = lambda xs: sum(x[0] for x in xs) / len(xs)
+    cycles = mean(gui) / N_XCD                                 # GRBM_GUI_ACTIVE sums the eight XCDs
+    dur_ns = sum(x[2] - x[1] for x in gui) / len(gui)
+    calib_bytes = CALIB_MIB << 20                              # the copy reads and writes this much
+    f_factor = calib_bytes / 1024.0 / cf[-1][0]
+    w_factor = calib_bytes / 1024.0 / cw[-1][0]
+    fetch_b = mean(fetch) * 1024.0 * f_factor
+    write_b = mean(write) * 1024.0 * w_factor
+    return {
+        "kernel": gui[0][3], "launches": len(gui), "kernel_source_hash": kernel_source_hash(),
+        "mfma_busy": round(mean(mfma) / (N_SIMD_TOTAL * cycles), 4),
+        "lds_bank_conflict_share": round(mean(bank) / max(mean(lds), 1.0), 4),
+        "gui_cycles_per_launch": round(cycles),
+        "kernel_ms_under_profiler": round(dur_ns / 1e6, 4),
+        "hbm_fetch_bytes_per_launch": round(fetch_b), "hbm_write_bytes_per_launch": round(write_b),
+        "hbm_bytes_per_launch": round(fetch_b + write_b),
+        "calibration": {"kernel": cf[-1][3], "bytes_read_and_written": calib_bytes,
+                        "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4)},
+        "definitions": "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE/8); "
+                       "LDS bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; "
+                       "HBM bytes = FETCH_SIZE, WRITE_SIZE (KiB) x the factor that maps the 1 GiB copy's reading "
+                       "to 1 GiB; means over the launches of each pass",
+    }
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -104,7 +223,10 @@ def cpu_baseline(w, q, k, v, budget_s: float):
             break
     dt = time.perf_counter() - t0
     flops = w.flops() * done / (w.B * w.H * w.N)      # same counting convention, pro rata per row
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "cores_note": "BLAS threads of the oracle's float64 products (the threads it used); "
+                          f"the process may run on {len(os.sched_getaffinity(0))} cores",
+            "kind": "oracle",
             "sample": f"{done} query rows (every {stride}th row of {heads} head(s), all {w.N} keys each, "
                       f"float64 numpy) in {dt:.1f} s; TFLOP/s counted like the GPU figure, pro rata per row",
             "seconds": round(dt, 2), "cpu_model": _cpu_model()}
@@ -350,6 +472,10 @@ def main():
                     help="skip the per-workload object (fp32, the two small-d shapes, the B=4 N=4096 shape)")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline fa_fwd (no split-KV, block-sparse or backward objects)")
+    ap.add_argument("--no-counters", action="store_true", help="skip the rocprofv3 counter passes")
+    ap.add_argument("--counter-dir", default=None, help="keep the counter passes' raw output here")
+    ap.add_argument("--write-profile", default=None, help="write the counter summary (JSON) to this file")
+    ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
@@ -357,14 +483,24 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    from tiled_attention_13_amd.inputs import WORKLOADS, digest, make_inputs
+    w = WORKLOADS[args.workload]
+    if args.counter_child:           # one counter pass: the calls and the calibration copy only
+        args.headline_only, args.no_cpu_baseline, args.no_counters = True, True, True
+    counters = None
+    if not args.no_counters:
+        # child processes first: this process has not touched the GPU yet
+        counters = collect_counters(w, keep_dir=args.counter_dir)
+        if args.write_profile and "error" not in counters:
+            with open(args.write_profile, "w") as fh:
+                json.dump({"workload": w.name, **counters}, fh, indent=1)
+
     import torch
     from tiled_attention_13_amd import fwd, load
-    from tiled_attention_13_amd.inputs import WORKLOADS, digest, make_inputs
 
     load()
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
-    w = WORKLOADS[args.workload]
     t_gen = time.perf_counter()
     q, k, v = make_inputs(w)
     gen_s = time.perf_counter() - t_gen
@@ -403,12 +539,23 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.counter_child:
+        return
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(per_call.mean())
     achieved = flops / (kern_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(w.name)
+    if counters is None or "error" in counters:
+        committed = committed_counters(w.name)
+        if committed is not None:
+            committed = {**committed, "source": "committed summary taken on these kernel sources"}
+        counters = committed or counters
+    traffic = counters.get("hbm_bytes_per_launch") if counters and "error" not in counters else None
+    if traffic is not None:
+        # counter cycles over the live kernel time: the clock the timed calls ran at (if it held)
+        counters = {**counters, "shader_clock_ghz_est": round(counters["gui_cycles_per_launch"] / (kern_ms * 1e6), 3),
+                    "hbm_gbps": round(traffic / (kern_ms * 1e-3) / 1e9, 1)}
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -431,8 +578,11 @@ def main():
         "hbm_gbps_compulsory": round(w.compulsory_bytes() / (kern_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "fwd_pp_kernel<d=128, causal, bf16> (one launch per fa_fwd call)",
-                     "per_launch_flops": flops},
+                     "kernel": f"{kernel_match(w)}, ...> (the only launch of a {w.dtype} fa_fwd call)"
+                               if w.dtype in ("bf16", "f32") else f"{kernel_match(w)}, ...> (plus pre-passes)",
+                     "kernel_ms": round(kern_ms, 4), "per_launch_flops": flops,
+                     "algorithmic_bytes": w.compulsory_bytes()},
+        "counters": counters,
         "input_sha256": digest(q, k, v)[:16],
         "input_gen_s": round(gen_s, 2),
     }

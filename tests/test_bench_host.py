@@ -1,5 +1,5 @@
 """Host-side logic of bench.py (no GPU): the one-GPU guard, the counter
-summary's source check and the oracle baseline's report."""
+summary's source check, the counter derivation and the oracle baseline's report."""
 import json
 import os
 import subprocess
@@ -18,29 +18,56 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.stdout == ""                      # no JSON line for a run that did not happen
 
 
-def test_traffic_is_reported_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+def test_committed_counters_are_used_only_for_the_source_they_were_taken_on(tmp_path, monkeypatch):
     import bench
-    f = tmp_path / "traffic.json"
+    f = tmp_path / "counters.json"
     summary = {"workload": "c4_bf16", "kernel_source_hash": bench.kernel_source_hash(),
-               "hbm_bytes_per_launch": 1.5e9}
+               "hbm_bytes_per_launch": 1.5e9, "mfma_busy": 0.5}
     f.write_text(json.dumps(summary))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.measured_traffic("c4_bf16") == 1.5e9
-    assert bench.measured_traffic("c3_bf16") is None          # another workload
+    monkeypatch.setattr(bench, "COUNTER_FILE", str(f))
+    assert bench.committed_counters("c4_bf16")["hbm_bytes_per_launch"] == 1.5e9
+    assert bench.committed_counters("c3_bf16") is None         # another workload
     summary["kernel_source_hash"] = "0" * 16                   # counters taken on other sources
     f.write_text(json.dumps(summary))
-    assert bench.measured_traffic("c4_bf16") is None
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.json"))
-    assert bench.measured_traffic("c4_bf16") is None
+    assert bench.committed_counters("c4_bf16") is None
+    monkeypatch.setattr(bench, "COUNTER_FILE", str(tmp_path / "missing.json"))
+    assert bench.committed_counters("c4_bf16") is None
 
 
-def test_committed_traffic_summary_matches_the_current_sources():
+def _row(dispatch, kernel, counter, value, t0=1000, t1=3000):
+    return {"Dispatch_Id": str(dispatch), "Kernel_Name": kernel, "Counter_Name": counter,
+            "Counter_Value": str(value), "Start_Timestamp": str(t0), "End_Timestamp": str(t1)}
+
+
+def test_counter_figures_from_rocprof_rows():
+    """Derivation of MFMA busy, conflict share, clock and calibrated HBM bytes from pass rows."""
     import bench
-    with open(bench.TRAFFIC_FILE) as fh:
+    k = "void fa::(anonymous namespace)::fwd_pp_kernel<128, true, false, 0, false>(KParams)"
+    cp = "__amd_rocclr_copyBuffer"
+    gui = 8 * 4000                                    # 4000 cycles per XCD in 2000 ns: 2 GHz
+    core = []
+    for dsp in (1, 2):
+        core += [_row(dsp, k, "GRBM_GUI_ACTIVE", gui), _row(dsp, k, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * 1024 * 4000),
+                 _row(dsp, k, "SQ_LDS_BANK_CONFLICT", 10), _row(dsp, k, "SQ_LDS_IDX_ACTIVE", 1000)]
+    gib_kib = (1 << 30) / 1024
+    fetch = [_row(1, k, "FETCH_SIZE", 1000.0), _row(2, k, "FETCH_SIZE", 3000.0), _row(3, cp, "FETCH_SIZE", gib_kib / 2)]
+    write = [_row(1, k, "WRITE_SIZE", 100.0), _row(2, k, "WRITE_SIZE", 100.0), _row(3, cp, "WRITE_SIZE", gib_kib)]
+    r = bench.derive_counters({"core": core, "fetch": fetch, "write": write}, "fwd_pp_kernel<128, true, false, 0")
+    assert r["mfma_busy"] == 0.5 and r["lds_bank_conflict_share"] == 0.01
+    assert r["gui_cycles_per_launch"] == 4000 and r["kernel_ms_under_profiler"] == 0.002 and r["launches"] == 2
+    assert r["calibration"]["fetch_factor"] == 2.0 and r["calibration"]["write_factor"] == 1.0
+    assert r["hbm_fetch_bytes_per_launch"] == 2000 * 1024 * 2 and r["hbm_write_bytes_per_launch"] == 100 * 1024
+    assert r["hbm_bytes_per_launch"] == r["hbm_fetch_bytes_per_launch"] + r["hbm_write_bytes_per_launch"]
+
+
+def test_committed_counter_summary_matches_the_current_sources():
+    import bench
+    with open(bench.COUNTER_FILE) as fh:
         t = json.load(fh)
     assert t["kernel_source_hash"] == bench.kernel_source_hash(), \
-        "profiles/fa_fwd_c4_bf16_traffic.json was taken on other kernel sources: re-take FETCH_SIZE/WRITE_SIZE"
+        "profiles/fa_fwd_c4_bf16_counters.json was taken on other kernel sources: re-take it (bench.py --write-profile)"
     assert t["hbm_bytes_per_launch"] == t["hbm_fetch_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+    assert 0.0 < t["mfma_busy"] < 1.0 and 0.0 <= t["lds_bank_conflict_share"] < 1.0
 
 
 def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
