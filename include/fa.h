@@ -61,7 +61,10 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
+
+/* Size of the static device buffer behind fa_fwd_splitkv_noalloc (per GPU). */
+#define FA_NOALLOC_SCRATCH_BYTES (128u << 20)
 
 typedef enum {
     FA_F32 = 0,       /* q, k, v, o float32; products and softmax in fp32 */
@@ -94,6 +97,7 @@ typedef enum {
     FA_ERR_OUT_OF_MEMORY = 9,
     FA_ERR_LAUNCH = 10,
     FA_ERR_HIP = 11,
+    FA_ERR_SCRATCH_LIMIT = 12,    /* problem too large for fa_fwd_splitkv_noalloc */
     /* not statuses: any int is a valid value of the enumeration */
     FA_STATUS_MIN_ENUM = -0x7FFFFFFF - 1,
     FA_STATUS_MAX_ENUM = 0x7FFFFFFF
@@ -211,6 +215,26 @@ fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
                          int64_t n_splits, void* stream);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, kernels and results (bit for bit)
+ * as fa_fwd_splitkv, but the partial O and lse live in a static device buffer
+ * of the library, FA_NOALLOC_SCRATCH_BYTES (128 MiB) on each GPU it runs on,
+ * held until the process ends.  The call makes no hipMalloc, hipFree or
+ * memset; the caller still passes the inputs and o / lse.
+ *   Limit: n_splits*B*H*N*d*4 + n_splits*B*H*N*4 bytes, each part rounded up
+ *   to 256, must not exceed FA_NOALLOC_SCRATCH_BYTES, else
+ *   FA_ERR_SCRATCH_LIMIT (checked before any HIP call).
+ *   Every call on one GPU uses that GPU's single buffer, which keeps the last
+ *   call's contents (nothing in it needs clearing: a call writes every entry
+ *   it reads).  Calls that overlap on one GPU -- on several streams, or from
+ *   several host threads -- race on it and give wrong results: serialise them.
+ */
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
+                                 int64_t n_splits, void* stream);
 
 /*
  * fa_fwd_blocksparse -- bf16 attention where only the blocks a 0/1 table

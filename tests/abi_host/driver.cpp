@@ -106,6 +106,18 @@ int main() {
         expect(fa_fwd_splitkv(q, k, v, o, lse, 1, 2, 1000, 128, 1, 0.1f, n, nullptr), FA_ERR_INVALID_ARGUMENT,
                "splitkv splits");
     expect_not_ok(fa_fwd_splitkv(q, k, v, o, lse, 1, 2, 1000, 128, 1, 0.1f, 3, nullptr), "splitkv valid");
+    for (int64_t n : {int64_t{0}, int64_t{1025}, kMax, kMin})
+        expect(fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 2, 1000, 128, 1, 0.1f, n, nullptr), FA_ERR_INVALID_ARGUMENT,
+               "splitkv_noalloc splits");
+    expect(fa_fwd_splitkv_noalloc(q, k, v, o, lse, kMax, kMax, 1000, 128, 1, 0.1f, 2, nullptr), FA_ERR_INVALID_SHAPE,
+           "splitkv_noalloc shape");
+    // 2 x 4 x 16384 x (128 + 1) x 4 bytes fit the 128 MiB buffer; 3 x 8 x 16384 ... do not
+    expect(fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 8, 16384, 128, 1, 0.1f, 3, nullptr), FA_ERR_SCRATCH_LIMIT,
+           "splitkv_noalloc limit");
+    expect(fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 1, 1 << 20, 128, 1, 0.1f, 1024, nullptr), FA_ERR_SCRATCH_LIMIT,
+           "splitkv_noalloc limit, many splits");
+    expect_not_ok(fa_fwd_splitkv_noalloc(q, k, v, o, lse, 1, 4, 16384, 128, 1, 0.1f, 2, nullptr),
+                  "splitkv_noalloc valid");
 
     // block-sparse
     const uint8_t* mask = static_cast<const uint8_t*>(P(0xC0000));

@@ -3,6 +3,7 @@
 // address and undefined-behaviour sanitizers: every launcher reports a failed
 // launch without enqueuing anything.
 #include "fa_internal.h"
+#include "fa_scratch.h"
 
 namespace fa {
 hipError_t launch_bs_plan(const uint8_t*, long long, int, int, bool, uint32_t*, int*, hipStream_t) {
@@ -18,4 +19,8 @@ hipError_t launch_quant_v_pow2(const void*, uint8_t*, uint8_t*, int, int, int, h
     return hipErrorInvalidValue;
 }
 hipError_t launch_quant_fp8(const void*, uint8_t*, float*, int, int, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t scratch_address(void** out) {
+    *out = nullptr;
+    return hipErrorNoDevice;
+}
 }  // namespace fa

@@ -175,3 +175,24 @@ def test_quant_v_pow2_rejects_bad_arguments(lib):
     assert q(P, P, P, 0, 64, 64, None) == 2
     assert q(P, P, P, 1, 64, 48, None) == 3
     assert q(P + 2, P, P, 1, 64, 64, None) == 6
+
+
+def test_splitkv_noalloc_rejects_bad_arguments_and_oversized_problems(lib):
+    """The no-allocation split-KV entry point checks what fa_fwd_splitkv checks,
+    and refuses (FA_ERR_SCRATCH_LIMIT = 12) a problem whose partial results
+    exceed its static buffer, before any HIP call."""
+    P = FAKE
+    q, k, v, o, l = P, P + 0x1000, P + 0x2000, P + 0x3000, P + 0x4000
+    f = lib.fa_fwd_splitkv_noalloc
+    assert f(q, k, v, 0, None, 1, 1, 128, 64, 0, 0.1, 2, None) == 1
+    assert f(q, k, v, o, None, 1, 1, 128, 64, 0, 0.1, 0, None) == 7
+    assert f(q, k, v, o, None, 1, 1, 128, 64, 0, 0.1, 1025, None) == 7
+    assert f(q, k, v, q, None, 1, 1, 128, 64, 0, 0.1, 2, None) == 7
+    assert f(q, k, v, o, None, 1, 1, 128, 48, 0, 0.1, 2, None) == 3
+    assert f(q, k, v, o, l + 2, 1, 1, 128, 64, 0, 0.1, 2, None) == 6
+    m = re.search(r"#define\s+FA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    # 3 splits x 8 heads x 16384 rows x (128 + 1) floats: over the limit
+    assert 3 * 8 * 16384 * 129 * 4 > limit
+    assert f(q, k, v, o, None, 1, 8, 16384, 128, 1, 0.1, 3, None) == 12
+    assert lib.fa_status_string(12).decode().startswith("the partial results need more")

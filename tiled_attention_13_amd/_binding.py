@@ -27,6 +27,7 @@ SIGNATURES = {
     "fa_fwd_partial": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _F, _P]),
     "fa_merge": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "fa_fwd_splitkv": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I64, _P]),
+    "fa_fwd_splitkv_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I64, _P]),
     "fa_fwd_blocksparse": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _I, _F, _P]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I, _F, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -286,6 +287,26 @@ def fwd_splitkv(q, k, v, n_splits: int, causal: bool = False, softmax_scale: flo
     st = load().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
                                int(bool(causal)), scale, int(n_splits), _stream_ptr(stream))
     _check(st, "fa_fwd_splitkv")
+    return out, lse
+
+
+def fwd_splitkv_noalloc(q, k, v, n_splits: int, out, lse=None, causal: bool = False,
+                        softmax_scale: float | None = None, stream=None):
+    """``fa_fwd_splitkv_noalloc``: the split-KV forward with its partial results
+    in the library's static device buffer, so the call allocates nothing (for
+    graph capture or loops that must not allocate).  The caller passes ``out``
+    (bf16 like q) and optionally ``lse`` (float32 [B, H, N]); calls that overlap
+    on one GPU race on the shared buffer.  Returns ``(out, lse)``."""
+    import torch
+    _check_qkv(q, k, v, torch.bfloat16)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    _check_out("out", out, q.shape, torch.bfloat16, q.device)
+    if lse is not None:
+        _check_out("lse", lse, (B, H, N), torch.float32, q.device)
+    st = load().fa_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d,
+                                       int(bool(causal)), scale, int(n_splits), _stream_ptr(stream))
+    _check(st, "fa_fwd_splitkv_noalloc")
     return out, lse
 
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_scratch.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept out of the generated code; the host pass

@@ -17,6 +17,7 @@
 #include <cstring>
 
 #include "fa_internal.h"
+#include "fa_scratch.h"
 
 namespace {
 
@@ -89,6 +90,57 @@ fa_status ws_alloc(void** p, size_t bytes, hipStream_t s) {
 
 hipError_t ws_free(void* p, hipStream_t s) { return p ? hipFreeAsync(p, s) : hipSuccess; }
 
+// Split-KV: argument checks shared by both entry points, the byte layout of
+// the partial results, and the launches on a caller-provided buffer.
+fa_status splitkv_check(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                        int64_t N, int64_t d, int causal, float softmax_scale, int64_t n_splits) {
+    if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+    fa_status st = check_shape(B, H, N, d);
+    if (st != FA_OK) return st;
+    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
+    if (n_splits < 1 || n_splits > kMaxParts) return FA_ERR_INVALID_ARGUMENT;
+    if (o == q || o == k || o == v) return FA_ERR_INVALID_ARGUMENT;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
+        return FA_ERR_MISALIGNED;
+    return FA_OK;
+}
+
+struct SplitLayout {
+    size_t off_lse, total;     // partial O at 0 (fp32 [n_splits, BH, N, d]), lse at off_lse
+};
+
+SplitLayout splitkv_layout(int64_t B, int64_t H, int64_t N, int64_t d, int64_t n_splits) {
+    const size_t rows = static_cast<size_t>(B) * static_cast<size_t>(H) * static_cast<size_t>(N);
+    const size_t off_lse = round_up(static_cast<size_t>(n_splits) * rows * static_cast<size_t>(d) * 4, 256);
+    return {off_lse, off_lse + round_up(static_cast<size_t>(n_splits) * rows * 4, 256)};
+}
+
+hipError_t splitkv_launch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                          int64_t N, int64_t d, int causal, float softmax_scale, int64_t n_splits, uint8_t* base,
+                          hipStream_t s) {
+    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
+    const int n_tiles = (n + fa::kKeyTile - 1) / fa::kKeyTile;
+    const int tps = (n_tiles + static_cast<int>(n_splits) - 1) / static_cast<int>(n_splits);
+    const SplitLayout lay = splitkv_layout(B, H, N, d, n_splits);
+    float* o32 = reinterpret_cast<float*>(base);
+    float* lse_part = reinterpret_cast<float*>(base + lay.off_lse);
+    // every (split, row) entry of o32 and lse_part is written by the partial
+    // kernel (rows that see no key of a split get O = 0, lse = -inf) before the
+    // merge reads it, so the buffer needs no clearing
+    fa::FwdArgs a{fa::Kind::BF16, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
+    a.o32 = o32;
+    a.lse_part = lse_part;
+    a.kt_lo = 0;
+    a.kt_hi = n_tiles;
+    a.tps = tps;
+    a.n_splits = static_cast<int>(n_splits);
+    hipError_t e = fa::launch_fwd(a, s);
+    if (e == hipSuccess) e = fa::launch_merge(o32, lse_part, static_cast<int>(n_splits), o, lse, BH, n, dd, s);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +159,9 @@ const char* fa_status_string(fa_status s) {
         case FA_ERR_OUT_OF_MEMORY: return "device workspace allocation failed";
         case FA_ERR_LAUNCH: return "kernel launch failed";
         case FA_ERR_HIP: return "HIP runtime call failed";
+        case FA_ERR_SCRATCH_LIMIT:
+            return "the partial results need more than the library's static scratch buffer "
+                   "(FA_NOALLOC_SCRATCH_BYTES); use fewer splits or the allocating entry point";
     }
     return "unknown status";
 }
@@ -283,45 +338,31 @@ fa_status fa_merge(const float* o_parts, const float* lse_parts, int64_t n_parts
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
                          int64_t n_splits, void* stream) {
-    if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
-    fa_status st = check_shape(B, H, N, d);
+    fa_status st = splitkv_check(q, k, v, o, lse, B, H, N, d, causal, softmax_scale, n_splits);
     if (st != FA_OK) return st;
-    if ((st = check_scale(softmax_scale)) != FA_OK) return st;
-    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARGUMENT;
-    if (n_splits < 1 || n_splits > kMaxParts) return FA_ERR_INVALID_ARGUMENT;
-    if (o == q || o == k || o == v) return FA_ERR_INVALID_ARGUMENT;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || (lse && !aligned(lse, 4)))
-        return FA_ERR_MISALIGNED;
     if ((st = check_device()) != FA_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
-    const int n_tiles = (n + fa::kKeyTile - 1) / fa::kKeyTile;
-    const int tps = (n_tiles + static_cast<int>(n_splits) - 1) / static_cast<int>(n_splits);
-    const size_t rows = static_cast<size_t>(BH) * n;
-    const size_t off_o32 = 0;
-    const size_t off_lse = off_o32 + round_up(static_cast<size_t>(n_splits) * rows * dd * 4, 256);
-    const size_t total = off_lse + round_up(static_cast<size_t>(n_splits) * rows * 4, 256);
     void* ws = nullptr;
-    if ((st = ws_alloc(&ws, total, s)) != FA_OK) return st;
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    float* o32 = reinterpret_cast<float*>(base + off_o32);
-    float* lse_part = reinterpret_cast<float*>(base + off_lse);
-    hipError_t e = hipSuccess;
-    {
-        fa::FwdArgs a{fa::Kind::BF16, q, k, v, nullptr, nullptr, nullptr, nullptr, nullptr,
-                      BH, n, padded_keys(n), dd, causal == 1, softmax_scale};
-        a.o32 = o32;
-        a.lse_part = lse_part;
-        a.kt_lo = 0;
-        a.kt_hi = n_tiles;
-        a.tps = tps;
-        a.n_splits = static_cast<int>(n_splits);
-        e = fa::launch_fwd(a, s);
-    }
-    if (e == hipSuccess) e = fa::launch_merge(o32, lse_part, static_cast<int>(n_splits), o, lse, BH, n, dd, s);
+    if ((st = ws_alloc(&ws, splitkv_layout(B, H, N, d, n_splits).total, s)) != FA_OK) return st;
+    const hipError_t e = splitkv_launch(q, k, v, o, lse, B, H, N, d, causal, softmax_scale, n_splits,
+                                        static_cast<uint8_t*>(ws), s);
     const hipError_t ef = ws_free(ws, s);
     if (e != hipSuccess) return launch_status(e);
     return ef == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, int causal, float softmax_scale,
+                                 int64_t n_splits, void* stream) {
+    fa_status st = splitkv_check(q, k, v, o, lse, B, H, N, d, causal, softmax_scale, n_splits);
+    if (st != FA_OK) return st;
+    if (splitkv_layout(B, H, N, d, n_splits).total > static_cast<size_t>(FA_NOALLOC_SCRATCH_BYTES))
+        return FA_ERR_SCRATCH_LIMIT;
+    if ((st = check_device()) != FA_OK) return st;
+    void* base = nullptr;
+    if (fa::scratch_address(&base) != hipSuccess) return FA_ERR_HIP;
+    return launch_status(splitkv_launch(q, k, v, o, lse, B, H, N, d, causal, softmax_scale, n_splits,
+                                        static_cast<uint8_t*>(base), static_cast<hipStream_t>(stream)));
 }
 
 fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
