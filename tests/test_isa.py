@@ -36,14 +36,24 @@ def isa(request, tmp_path_factory):
 
 
 def test_m0_only_set_by_tile_copies(isa):
+    """Every M0 write is `s_mov_b32 m0, sN` or `s_add_u32 m0, sN, imm`, followed by
+    the LDS-DMA load (with an optional `s_mov_b32 sK, imm` for its scalar offset)."""
     lines = [l.strip() for l in isa]
     copies = 0
     for i, l in enumerate(lines):
         if l.startswith(";") or not re.search(r"\bm0\b", l):
             continue
-        assert re.match(r"s_mov_b32 m0, s\d+$", l), f"M0 used outside a tile copy: {l}"
-        assert re.match(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], 0 offen lds$", lines[i + 1]), \
-            f"M0 write not followed by an LDS-DMA load: {l} / {lines[i + 1]}"
+        assert re.match(r"(s_mov_b32 m0, s\d+|s_add_u32 m0, s\d+, (0x[0-9a-f]+|\d+))$", l), \
+            f"M0 used outside a tile copy: {l}"
+        nxt = lines[i + 1]
+        so = re.match(r"s_mov_b32 (s\d+), (0x[0-9a-f]+|\d+)$", nxt)
+        if so:
+            nxt = lines[i + 2]
+            assert re.match(rf"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], {so.group(1)} offen lds$", nxt), \
+                f"M0 write not followed by an LDS-DMA load: {l} / {lines[i + 1]} / {nxt}"
+        else:
+            assert re.match(r"buffer_load_dwordx4 v\d+, s\[\d+:\d+\], 0 offen lds$", nxt), \
+                f"M0 write not followed by an LDS-DMA load: {l} / {nxt}"
         copies += 1
     assert copies > 0, "no LDS-DMA tile copies found"
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 namespace {
 
@@ -101,7 +103,31 @@ __device__ __forceinline__ void lds_dma16(uint32_t lds, u32x4 rsrc, uint32_t vof
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds), "v"(voff), "s"(rsrc)
                  : "memory");
 }
+// The same copy with compile-time offsets: LDS byte lds + LDS_OFF, source
+// offset voff + SRC_OFF (SRC_OFF through the instruction's scalar offset).
+// Only the base addresses occupy registers, so a loop over many blocks keeps
+// nothing per block live.
+template <int LDS_OFF, int SRC_OFF>
+__device__ __forceinline__ void lds_dma16_at(uint32_t lds, u32x4 rsrc, uint32_t voff) {
+    if constexpr (SRC_OFF == 0) {
+        asm volatile("s_add_u32 m0, %0, %3\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     : : "s"(lds), "v"(voff), "s"(rsrc), "i"(LDS_OFF) : "memory", "scc");
+    } else {
+        uint32_t so;
+        asm volatile("s_add_u32 m0, %1, %4\n\ts_mov_b32 %0, %5\n\tbuffer_load_dwordx4 %2, %3, %0 offen lds"
+                     : "=&s"(so) : "s"(lds), "v"(voff), "s"(rsrc), "i"(LDS_OFF), "i"(SRC_OFF) : "memory", "scc");
+    }
+}
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, each a compile-time constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // Buffer resource words for a byte range [base, base + bytes) (the layout
 // __builtin_amdgcn_make_buffer_rsrc builds), for the inline-assembly copies.

@@ -764,6 +764,286 @@ void fwd_pp_kernel(KParams p) {
 }
 
 // ===========================================================================
+// bf16, d = 128: the same ping-pong schedule with 128 keys per slot
+//
+// Each matrix-core slot covers 128 keys (64 MFMAs per wave instead of 32), so
+// the fixed cost of a slot -- the wait for the first LDS operands, the
+// barrier -- is paid once per 128 keys.  K and V tiles live in two separate
+// double-buffered rings (K 128 x 272 B, V 128 x 256 B per stage: 132 KiB):
+// K_t is read by S_t in slots 2t (group A) and 2t+1 (group B), V_t by PV_t in
+// slots 2t+2 and 2t+3.  Group B copies both, in its vector slot 2j+2: K_{j+2}
+// into the stage K_j left (last read in slot 2j+1) and V_{j+1} into the stage
+// V_{j-1} left (last read in slot 2j+1); it waits for them at the end of slot
+// 2j+3, before the barrier after which group A first reads them.  Copies are
+// LDS-DMA blocks of 1 KiB as in the 64-key kernel.
+// ===========================================================================
+struct B128Cfg {
+    static constexpr int D = 128, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 128;
+    static constexpr int KROW = D * 2 + 16, VROW = D * 2;
+    // a K stage holds 34 KiB of padded rows; it is rounded up to 36 blocks so
+    // that each of the four copying waves issues the same nine (the last two
+    // blocks carry no data)
+    static constexpr int K_BLOCKS = (BN * KROW + 4095) / 4096 * 4, V_BLOCKS = BN * VROW / 1024;
+    static constexpr int KSTAGE = K_BLOCKS * 1024, VSTAGE = V_BLOCKS * 1024;   // 36 KiB, 32 KiB
+    static constexpr int K_PER_W = K_BLOCKS / 4, V_PER_W = V_BLOCKS / 4;
+    static constexpr int QREGS = D / 16;
+    static constexpr int SMEM = 2 * KSTAGE + 2 * VSTAGE;
+};
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void fwd_b128_kernel(KParams p) {
+    using C = B128Cfg;
+    constexpr int D = C::D, BM = C::BM, BN = C::BN;
+    static_assert(C::KSTAGE % 1024 == 0 && C::VSTAGE % 4096 == 0, "LDS-DMA layout");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, grp = w >> 2, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    int qt = blockIdx.x / p.BH;
+    const int bh = blockIdx.x - qt * p.BH;
+    if (CAUSAL) qt = p.n_qtiles - 1 - qt;        // heaviest query tiles first
+    const int q0 = qt * BM, qw0 = q0 + 32 * w, my_q = qw0 + l32;
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* qg = p.q + slice * 2;
+    const uint8_t* kg = p.k + slice * 2;
+    const uint8_t* vg = p.v + slice * 2;
+
+    u32x4 qf[C::QREGS];
+    {
+        const bool ok = my_q < N;
+        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * 2;
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i) qf[i] = ok ? ld16(row + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+    }
+
+    const int n_all = (N + BN - 1) / BN;
+    const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
+    // last key tile with a key at or before this wave's last query
+    const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
+
+    // ---- tile copies (group B): per-lane source offsets of its K blocks (padded
+    // rows: 16 granules + one pad granule) and of its first V block (V blocks
+    // of one wave are 16 key rows = 4 KiB of source apart)
+    const uint32_t smem_lds = lds_address(smem);
+    const uint32_t kbase = smem_lds, vbase = smem_lds + 2 * C::KSTAGE;
+    uint32_t k_off[C::K_PER_W];
+    uint32_t v_off0 = 0;
+    if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < C::K_PER_W; ++i)
+            k_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, D * 2 / 16, D * 2, BN);   // past row BN: no data
+        const int row = 4 * (w & 3) + (lane >> 4);
+        v_off0 = row * (D * 2) + 16 * v_granule<D>(row, lane & 15);
+    }
+    // block (w & 3) + 4i of a stage: LDS byte 1024 (w & 3) + 4096 i of it
+    auto copy_k = [&](int t) {                    // K_t into K stage t % 2
+        const int n0 = t * BN;
+        const u32x4 r = buffer_words(kg + static_cast<size_t>(n0) * D * 2, static_cast<uint32_t>(min(N - n0, BN) * D * 2));
+        const uint32_t st = kbase + (t & 1) * C::KSTAGE + 1024 * (w & 3);
+        static_for<0, C::K_PER_W>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            lds_dma16_at<4096 * i, 0>(st, r, k_off[i]);
+        });
+    };
+    auto copy_v = [&](int t) {                    // V_t into V stage t % 2; its rows 16 i further on
+        const int n0 = t * BN;
+        const u32x4 r = buffer_words(vg + static_cast<size_t>(n0) * D * 2, static_cast<uint32_t>(min(N - n0, BN) * D * 2));
+        const uint32_t st = vbase + (t & 1) * C::VSTAGE + 1024 * (w & 3);
+        static_for<0, C::V_PER_W>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            lds_dma16_at<4096 * i, 16 * i * C::VROW>(st, r, v_off0);
+        });
+    };
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] = 0.0f;
+    float m_run = kNegInf, l_run = 0.0f;
+    float s[BN / 2];
+    bf16x8 pf[BN / 16];
+
+    const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
+    uint32_t lane_vo[D / 32];
+    {
+        const int g = lane >> 4, r = (lane >> 2) & 3, j = lane & 3;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+            lane_vo[db] = (4 * (g >> 1) + r) * C::VROW + 64 * (db ^ r) + 16 * (2 * (g & 1) + (j >> 1)) + 8 * (j & 1);
+    }
+
+    // S^T = K_t Q^T over the 128 keys of tile t
+    auto op_s = [&](int t) {
+        const uint8_t* kl = lane_k + (t & 1) * C::KSTAGE;
+        constexpr int NA = (BN / 32) * C::QREGS;
+        bf16x8 a[NA];
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+                a[i * (BN / 32) + kb] = __builtin_bit_cast(bf16x8, ld16(kl + 32 * kb * C::KROW + 32 * i));
+        f32x16 acc[BN / 32];
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) acc[kb] = f32x16{};
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+                acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i * (BN / 32) + kb], __builtin_bit_cast(bf16x8, qf[i]),
+                                                                 acc[kb], 0, 0, 0);
+        pipeline_lds_mfma<NA, kLdsAhead>();
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[16 * kb + v] = acc[kb][v];
+    };
+    // O^T += V_t^T P_t^T
+    auto op_pv = [&](int t) {
+        constexpr int NA = (D / 32) * (BN / 16);
+        bf16x8 a[NA];
+        const lds_u8* vs = (const lds_u8*)smem + 2 * C::KSTAGE + (t & 1) * C::VSTAGE;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const lds_u8* vb = vs + lane_vo[db];
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc) {
+                const i16x4 lo = ds_read_tr16(vb + 16 * cc * C::VROW);
+                const i16x4 hi = ds_read_tr16(vb + (16 * cc + 8) * C::VROW);
+                a[db * (BN / 16) + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db * (BN / 16) + cc], pf[cc], o[db], 0, 0, 0);
+        pipeline_lds_mfma<NA, kLdsAhead, 2>();
+    };
+    // softmax of tile t, rescale of O, probabilities packed to bf16
+    auto op_softmax = [&](int t, bool masked) {
+        if (masked) {
+            // key t*BN + 4h + c is visible iff c <= lim
+            const int lim = (CAUSAL ? min(N - 1, my_q) : N - 1) - t * BN - 4 * h;
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (32 * kb + 8 * (v >> 2) + (v & 3) > lim) s[16 * kb + v] = kNegInf;   // acc_row(v, h) - 4h
+        }
+        const float alpha = softmax_step(s, p.c_log2, m_run, l_run);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+        }
+#pragma unroll
+        for (int cc = 0; cc < BN / 16; ++cc)
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) pf[cc][t8] = static_cast<__bf16>(s[8 * cc + t8]);
+    };
+    auto masked_tile = [&](int t) { return (CAUSAL && t * BN + BN - 1 > qw0) || t * BN + BN > N; };
+    // slot boundary: neither matrix-core nor vector work crosses it (left to
+    // itself the scheduler moves MFMAs into the vector slot and exps into the
+    // matrix slot, which measured slower)
+    auto slot_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: group B copies K_0 and waits; everyone meets at barrier 0
+    if (grp == 1) {
+        copy_k(0);
+        wait_lds_dma();
+    }
+    lds_barrier();
+
+    // Tiles before j_last need no mask (their last key precedes this wave's first
+    // query, and only the last tile can hold keys >= N); the masked tile j_last
+    // is peeled off the loops so that the masking code stays out of them.
+    const bool last_masked = masked_tile(j_last);
+    if (grp == 0) {
+        // A: M_0 | V_0 M_1 | ... | V_{n-1} M_n | idle
+        op_s(0);
+        slot_end();
+        for (int j = 0; j < j_last; ++j) {
+            op_softmax(j, false);
+            slot_end();
+            op_pv(j);
+            __builtin_amdgcn_sched_barrier(0);
+            op_s(j + 1);
+            slot_end();
+        }
+        op_softmax(j_last, last_masked);
+        slot_end();
+        op_pv(j_last);
+        slot_end();
+        for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: slots only
+            slot_end();
+            slot_end();
+        }
+        slot_end();
+    } else {
+        // B: copies | M_0 | V_0 + copies, M_1 | ... | V_{n-1} + copies, M_n
+        if (1 < n_kt) copy_k(1);
+        copy_v(0);
+        slot_end();
+        op_s(0);
+        wait_lds_dma();
+        slot_end();
+        auto copies = [&](int j) {
+            if (j + 2 < n_kt) copy_k(j + 2);
+            if (j + 1 < n_kt) copy_v(j + 1);
+        };
+        for (int j = 0; j < j_last; ++j) {
+            op_softmax(j, false);
+            copies(j);
+            slot_end();
+            op_pv(j);
+            __builtin_amdgcn_sched_barrier(0);
+            op_s(j + 1);
+            wait_lds_dma();
+            slot_end();
+        }
+        op_softmax(j_last, last_masked);
+        copies(j_last);
+        slot_end();
+        op_pv(j_last);
+        wait_lds_dma();
+        slot_end();
+        for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: copies for the others
+            copies(j);
+            slot_end();
+            wait_lds_dma();
+            slot_end();
+        }
+    }
+
+    // ---- epilogue
+    const float l_tot = sum_halves(l_run);
+    if (my_q < N) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint8_t* orow = p.o + (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(o[db][4 * g + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + 2 * (32 * db + 8 * g + 4 * h)) = out;
+            }
+        if (p.lse != nullptr && h == 0)
+            p.lse[static_cast<size_t>(bh) * N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ===========================================================================
 // fp32 kernel: same algorithm on the 32x32x2 fp32 MFMA (no reduced-precision
 // products, probabilities kept in fp32 for P*V).
 // ===========================================================================
@@ -1104,8 +1384,18 @@ __global__ __launch_bounds__(256) void quant_v_pow2_kernel(const uint8_t* __rest
 }
 
 
+template <bool CAUSAL>
+hipError_t launch_b128(KParams kp, int BH, hipStream_t st) {
+    kp.n_qtiles = (kp.N + B128Cfg::BM - 1) / B128Cfg::BM;
+    const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
+    if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((fwd_b128_kernel<CAUSAL>), dim3(static_cast<int>(grid)), dim3(B128Cfg::NT), 0, st, kp);
+    return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool FP8>
 hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
+    if constexpr (D == 128 && !FP8) return launch_b128<CAUSAL>(kp, BH, st);
     kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
