@@ -127,6 +127,8 @@ def kernel_match(w) -> str:
     """Substring of the attention kernel's name in rocprofv3 output for a workload."""
     if w.dtype == "f32":
         return "fwd_f32_kernel"
+    if w.dtype == "bf16" and w.d == 128:
+        return f"fwd_b128_kernel<{'true' if w.causal else 'false'}>"
     return f"fwd_pp_kernel<{w.d}, {'true' if w.causal else 'false'}, {'true' if w.dtype != 'bf16' else 'false'}, 0"
 
 
@@ -578,8 +580,8 @@ def main():
         "hbm_gbps_compulsory": round(w.compulsory_bytes() / (kern_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": f"{kernel_match(w)}, ...> (the only launch of a {w.dtype} fa_fwd call)"
-                               if w.dtype in ("bf16", "f32") else f"{kernel_match(w)}, ...> (plus pre-passes)",
+                     "kernel": f"{kernel_match(w)} (the only launch of a {w.dtype} fa_fwd call)"
+                               if w.dtype in ("bf16", "f32") else f"{kernel_match(w)} (plus pre-passes)",
                      "kernel_ms": round(kern_ms, 4), "per_launch_flops": flops,
                      "algorithmic_bytes": w.compulsory_bytes()},
         "counters": counters,

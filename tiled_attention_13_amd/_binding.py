@@ -45,19 +45,24 @@ def lib_path() -> str:
     return _LIB_PATH
 
 
+def load_library(path: str):
+    """Open a build of the C ABI at `path` with the signatures of include/fa.h."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not built: {path} is missing "
+                           "(run `python -m tiled_attention_13_amd.build`)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
 def load():
     """Load the library once; raise if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise RuntimeError(f"HIP library not built: {_LIB_PATH} is missing "
-                               "(run `python -m tiled_attention_13_amd.build`)")
-        lib = ctypes.CDLL(_LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = load_library(_LIB_PATH)
     return _lib
 
 

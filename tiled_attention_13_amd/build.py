@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+# the same library built with FA_POISON_STAGES=1: a race check for the LDS rings
+# (tests only; see poison_block in csrc/fa_device.h)
+LIB_POISONED = os.path.join(PKG, "libfa_poisoned.so")
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_scratch.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
@@ -33,21 +36,26 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def build(verbose: bool = False) -> str:
+def _build_one(out: str, extra: list, verbose: bool) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
         objs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
             if src.endswith(".cpp"):
                 cmd[1:1] = ["-x", "hip"]
             _run(cmd, verbose)
             objs.append(obj)
-        tmp_lib = os.path.join(tmp, "libfa.so")
+        tmp_lib = os.path.join(tmp, os.path.basename(out))
         _run([cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp_lib], verbose)
-        shutil.move(tmp_lib, LIB)   # atomic replace of the in-tree library
-    return LIB
+        shutil.move(tmp_lib, out)   # atomic replace of the in-tree library
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _build_one(LIB_POISONED, ["-DFA_POISON_STAGES=1"], verbose)
+    return _build_one(LIB, [], verbose)
 
 
 def _run(cmd, verbose):

@@ -182,7 +182,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
 #pragma unroll
         for (int i = 0; i < PER_W; ++i) {
             const int b = w + 8 * i;
-            if (i < dn) lds_dma16(stage + 1024 * b, b < NB_K ? kr : (b < 2 * NB_K ? vr : tr), doff[i]);
+            if (i < dn) {
+                poison_block(stage + 1024 * b);
+                lds_dma16(stage + 1024 * b, b < NB_K ? kr : (b < 2 * NB_K ? vr : tr), doff[i]);
+            }
         }
     };
 
@@ -358,7 +361,10 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
 #pragma unroll
         for (int i = 0; i < PER_W; ++i) {
             const int b = w + 8 * i;
-            if (i < dn) lds_dma16(stage + 1024 * b, b < NB_R ? rq : (b < C::NR * NB_R ? rg : rt), doff[i]);
+            if (i < dn) {
+                poison_block(stage + 1024 * b);
+                lds_dma16(stage + 1024 * b, b < NB_R ? rq : (b < C::NR * NB_R ? rg : rt), doff[i]);
+            }
         }
     };
     u32x4 vecst;

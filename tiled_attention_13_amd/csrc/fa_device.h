@@ -120,6 +120,24 @@ __device__ __forceinline__ void lds_dma16_at(uint32_t lds, u32x4 rsrc, uint32_t 
 }
 __device__ __forceinline__ void wait_lds_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Race-check build (compile with -DFA_POISON_STAGES=1): before a wave issues a
+// copy into a ring stage, it fills the 1 KiB LDS block the copy will land in
+// with NaN.  The poison goes in after the barrier that ends the last read of
+// the stage's previous tile; a read of the stage that lagged behind that
+// barrier, or ran ahead of the copy's wait, would see NaN instead of data, so
+// this build's outputs equal the normal build's bit for bit only if no such
+// race exists.
+#ifndef FA_POISON_STAGES
+#define FA_POISON_STAGES 0
+#endif
+__device__ __forceinline__ void poison_block(uint32_t lds) {
+    if constexpr (FA_POISON_STAGES != 0) {
+        const uint32_t addr = lds + 16u * (threadIdx.x & 63u);
+        const u32x4 nan = {0x7FC00000u, 0x7FC00000u, 0x7FC00000u, 0x7FC00000u};
+        asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : : "v"(addr), "v"(nan) : "memory");
+    }
+}
+
 // f(std::integral_constant<int, I>) for I = B .. E-1, each a compile-time constant.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

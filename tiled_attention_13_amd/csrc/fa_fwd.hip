@@ -396,6 +396,7 @@ void fwd_pp_kernel(KParams p) {
         for (int i = 0; i < DMA_PER_W; ++i) {
             if (i < dma_n) {
                 const int b = b0 + 4 * i;
+                poison_block(stage + 1024 * b);
                 lds_dma16(stage + 1024 * b, b < DMA_K ? kr : vr, dma_off[i]);
             }
         }
@@ -788,6 +789,7 @@ struct B128Cfg {
     static constexpr int K_PER_W = K_BLOCKS / 4, V_PER_W = V_BLOCKS / 4;
     static constexpr int QREGS = D / 16;
     static constexpr int SMEM = 2 * KSTAGE + 2 * VSTAGE;
+    static constexpr int AHEAD = 9;            // LDS operand lookahead, in MFMAs (9 measured 0.7 % faster than 6)
 };
 
 template <bool CAUSAL>
@@ -845,6 +847,7 @@ void fwd_b128_kernel(KParams p) {
         const uint32_t st = kbase + (t & 1) * C::KSTAGE + 1024 * (w & 3);
         static_for<0, C::K_PER_W>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
+            poison_block(st + 4096 * i);
             lds_dma16_at<4096 * i, 0>(st, r, k_off[i]);
         });
     };
@@ -854,6 +857,7 @@ void fwd_b128_kernel(KParams p) {
         const uint32_t st = vbase + (t & 1) * C::VSTAGE + 1024 * (w & 3);
         static_for<0, C::V_PER_W>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
+            poison_block(st + 4096 * i);
             lds_dma16_at<4096 * i, 16 * i * C::VROW>(st, r, v_off0);
         });
     };
@@ -895,7 +899,7 @@ void fwd_b128_kernel(KParams p) {
             for (int kb = 0; kb < BN / 32; ++kb)
                 acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i * (BN / 32) + kb], __builtin_bit_cast(bf16x8, qf[i]),
                                                                  acc[kb], 0, 0, 0);
-        pipeline_lds_mfma<NA, kLdsAhead>();
+        pipeline_lds_mfma<NA, C::AHEAD>();
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
@@ -921,7 +925,7 @@ void fwd_b128_kernel(KParams p) {
 #pragma unroll
             for (int cc = 0; cc < BN / 16; ++cc)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[db * (BN / 16) + cc], pf[cc], o[db], 0, 0, 0);
-        pipeline_lds_mfma<NA, kLdsAhead, 2>();
+        pipeline_lds_mfma<NA, C::AHEAD, 2>();
     };
     // softmax of tile t, rescale of O, probabilities packed to bf16
     auto op_softmax = [&](int t, bool masked) {
