@@ -4,8 +4,9 @@ into it is issued, i.e. just after the barrier that ends the last read of
 the stage's previous tile.  A read that lagged behind that barrier or ran
 ahead of the copy's wait would see NaN; with no such race both builds give the
 same bits.  Covered: the bf16 d=128 forward (128-key slots, separate K and V
-rings), the 64-key LDS-DMA kernels (FP8, FP8 P*V, split-KV partials) and the
-backward's dK/dV and dQ rings, at small ragged shapes spanning several tiles."""
+rings), the 64-key LDS-DMA kernels (bf16 at d = 32 and 64, FP8, FP8 P*V,
+split-KV partials) and the backward's dK/dV and dQ rings, at d = 32, 64 and
+128 and small ragged shapes spanning several tiles."""
 import os
 
 import pytest
@@ -37,10 +38,11 @@ def _with_lib(lib, fn):
 
 @pytest.mark.parametrize("path", ["bf16", "fp8", "fp8pv", "splitkv", "bwd"])
 @pytest.mark.parametrize("causal", [False, True])
-def test_poisoned_build_gives_the_same_bits(gpu_lib, poisoned, path, causal):
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_poisoned_build_gives_the_same_bits(gpu_lib, poisoned, path, causal, d):
     import torch
     import tiled_attention_13_amd as fa
-    w = Workload("poison", 1, 3, 1000 + 37, 128, "bf16", causal, 97)
+    w = Workload("poison", 1, 3, 1000 + 37, d, "bf16", causal, 97)
     q, k, v = make_inputs(w)
     tq, tk, tv = (to_device(a, "bf16") for a in (q, k, v))
     if path == "bwd":

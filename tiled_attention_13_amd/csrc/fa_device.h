@@ -99,9 +99,11 @@ __device__ __forceinline__ void lds_barrier() {
 // naming it in the clobber list is not honoured (clang warns that reserved
 // registers may not be preserved), so correctness rests on nothing else in
 // these kernels using M0, which the ISA test checks on every build.
+// The LDS address is wave-uniform by construction (stage, block and wave
+// index); readfirstlane tells the compiler so.
 __device__ __forceinline__ void lds_dma16(uint32_t lds, u32x4 rsrc, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(lds), "v"(voff), "s"(rsrc)
-                 : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 : : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(rsrc) : "memory");
 }
 // The same copy with compile-time offsets: LDS byte lds + LDS_OFF, source
 // offset voff + SRC_OFF (SRC_OFF through the instruction's scalar offset).

@@ -197,11 +197,12 @@ struct PPCfg {
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;           // queries per workgroup
     static constexpr int BN = kKeyTile;          // keys per tile
-    // d = 128: K and V^T tiles go global -> LDS directly (buffer loads to LDS),
-    // issued a slot earlier than a register copy would store them, so the ring
-    // has a fourth stage.  Not in the block-sparse kernel: its short runs of
-    // listed tiles measured slower that way.
-    static constexpr bool DMA = D == 128 && MODE != kModeSparse;
+    // K and V tiles go global -> LDS directly (buffer loads to LDS), issued a
+    // slot earlier than a register copy would store them, so the ring has a
+    // fourth stage.  Not in the block-sparse kernel (its short runs of listed
+    // tiles measured slower that way), nor for the e4m3 V^T at d = 32 (its
+    // 2.5 KiB tile is not a whole number of 1 KiB copy blocks).
+    static constexpr bool DMA = MODE != kModeSparse && !(PV8 && D == 32);
     static constexpr int STAGES = DMA ? 4 : 3;
     static constexpr int ES = FP8 ? 1 : 2;       // bytes per Q/K element
     static constexpr int KROW = D * ES + 16;     // bytes per K row in LDS (padded)
