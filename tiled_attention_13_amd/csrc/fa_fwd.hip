@@ -118,6 +118,34 @@ __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m,
     return alpha;
 }
 
+// The same step for NS scores whose first and second halves are scaled into
+// base-2 units by different factors (c0, c1 > 0): the two 64-key halves of an
+// FP8 tile, each with its own K scale.
+template <int NS>
+__device__ __forceinline__ float softmax_step2(float (&s)[NS], float c0, float c1, float& m, float& l) {
+    float ma = kNegInf, mb = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) ma = fmaxf(ma, s[i]);
+#pragma unroll
+    for (int i = NS / 2; i < NS; ++i) mb = fmaxf(mb, s[i]);
+    const float mx2 = fmaxf(max_halves(ma) * c0, max_halves(mb) * c1);
+    float alpha = 1.0f;
+    if (mx2 > m + kRescaleSlack) {        // also taken on the first unmasked tile (m = -inf)
+        alpha = fast_exp2(m - mx2);
+        m = mx2;
+    }
+    const float m_use = (m == kNegInf) ? 0.0f : m;   // nothing unmasked yet: all p are 0
+    float rs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const float p = fast_exp2(fmaf(s[i], i < NS / 2 ? c0 : c1, -m_use));
+        s[i] = p;
+        rs += p;
+    }
+    l = fmaf(l, alpha, rs);
+    return alpha;
+}
+
 // Same step for an e4m3 P*V product: the probabilities come out multiplied by
 // 2^f, with f the largest integer (at most 127) for which this tile's largest
 // probability stays within the e4m3 range 448 (so they fill that range before
@@ -779,25 +807,28 @@ void fwd_pp_kernel(KParams p) {
 // 2j+3, before the barrier after which group A first reads them.  Copies are
 // LDS-DMA blocks of 1 KiB as in the 64-key kernel.
 // ===========================================================================
+template <bool FP8>
 struct B128Cfg {
     static constexpr int D = 128, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 128;
-    static constexpr int KROW = D * 2 + 16, VROW = D * 2;
-    // a K stage holds 34 KiB of padded rows; it is rounded up to 36 blocks so
-    // that each of the four copying waves issues the same nine (the last two
-    // blocks carry no data)
+    static constexpr int ES = FP8 ? 1 : 2;     // bytes per Q/K element (e4m3 or bf16)
+    static constexpr int KROW = D * ES + 16, VROW = D * 2;
+    // a K stage holds BN padded rows (34 KiB, e4m3 18 KiB); it is rounded up to
+    // whole groups of four blocks so that each of the four copying waves issues
+    // the same number (the last blocks carry no data)
     static constexpr int K_BLOCKS = (BN * KROW + 4095) / 4096 * 4, V_BLOCKS = BN * VROW / 1024;
-    static constexpr int KSTAGE = K_BLOCKS * 1024, VSTAGE = V_BLOCKS * 1024;   // 36 KiB, 32 KiB
+    static constexpr int KSTAGE = K_BLOCKS * 1024, VSTAGE = V_BLOCKS * 1024;
     static constexpr int K_PER_W = K_BLOCKS / 4, V_PER_W = V_BLOCKS / 4;
-    static constexpr int QREGS = D / 16;
+    // Q fragments per lane: 16 dims per bf16 MFMA; e4m3: 64 dims per MFMA, 32 bytes a lane
+    static constexpr int QREGS = FP8 ? 2 * (D / 64) : D / 16;
     static constexpr int SMEM = 2 * KSTAGE + 2 * VSTAGE;
     static constexpr int AHEAD = 9;            // LDS operand lookahead, in MFMAs (9 measured 0.7 % faster than 6)
 };
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool FP8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_b128_kernel(KParams p) {
-    using C = B128Cfg;
-    constexpr int D = C::D, BM = C::BM, BN = C::BN;
+    using C = B128Cfg<FP8>;
+    constexpr int D = C::D, BM = C::BM, BN = C::BN, ES = C::ES;
     static_assert(C::KSTAGE % 1024 == 0 && C::VSTAGE % 4096 == 0, "LDS-DMA layout");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
 
@@ -810,17 +841,24 @@ void fwd_b128_kernel(KParams p) {
     if (CAUSAL) qt = p.n_qtiles - 1 - qt;        // heaviest query tiles first
     const int q0 = qt * BM, qw0 = q0 + 32 * w, my_q = qw0 + l32;
     const size_t slice = static_cast<size_t>(bh) * N * D;
-    const uint8_t* qg = p.q + slice * 2;
-    const uint8_t* kg = p.k + slice * 2;
+    const uint8_t* qg = p.q + slice * ES;
+    const uint8_t* kg = p.k + slice * ES;
     const uint8_t* vg = p.v + slice * 2;
 
+    // Q fragments (B operand): bf16 dims 16i + 8h .. +7; e4m3 dims 64(i/2) + 32h + 16(i%2) .. +15
     u32x4 qf[C::QREGS];
     {
         const bool ok = my_q < N;
-        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * 2;
+        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * ES;
 #pragma unroll
-        for (int i = 0; i < C::QREGS; ++i) qf[i] = ok ? ld16(row + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < C::QREGS; ++i)
+            qf[i] = !ok ? u32x4{0, 0, 0, 0} : FP8 ? ld16(row + 64 * (i >> 1) + 32 * h + 16 * (i & 1)) : ld16(row + 2 * (16 * i + 8 * h));
     }
+    // scores in base-2 units: s * c (FP8: with the dequantisation 1/(q_scale k_scale),
+    // the K scale per 64-key half of a tile)
+    const int n_scale = (N + 63) / 64;
+    float c_q = p.c_log2;
+    if constexpr (FP8) c_q = p.c_log2 / p.q_scale[bh * n_scale + (qw0 < N ? qw0 : N - 1) / 64];
 
     const int n_all = (N + BN - 1) / BN;
     const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
@@ -837,14 +875,14 @@ void fwd_b128_kernel(KParams p) {
     if (grp == 1) {
 #pragma unroll
         for (int i = 0; i < C::K_PER_W; ++i)
-            k_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, D * 2 / 16, D * 2, BN);   // past row BN: no data
+            k_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, D * ES / 16, D * ES, BN);   // past row BN: no data
         const int row = 4 * (w & 3) + (lane >> 4);
         v_off0 = row * (D * 2) + 16 * v_granule<D>(row, lane & 15);
     }
     // block (w & 3) + 4i of a stage: LDS byte 1024 (w & 3) + 4096 i of it
     auto copy_k = [&](int t) {                    // K_t into K stage t % 2
         const int n0 = t * BN;
-        const u32x4 r = buffer_words(kg + static_cast<size_t>(n0) * D * 2, static_cast<uint32_t>(min(N - n0, BN) * D * 2));
+        const u32x4 r = buffer_words(kg + static_cast<size_t>(n0) * D * ES, static_cast<uint32_t>(min(N - n0, BN) * D * ES));
         const uint32_t st = kbase + (t & 1) * C::KSTAGE + 1024 * (w & 3);
         static_for<0, C::K_PER_W>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
@@ -884,6 +922,40 @@ void fwd_b128_kernel(KParams p) {
     // S^T = K_t Q^T over the 128 keys of tile t
     auto op_s = [&](int t) {
         const uint8_t* kl = lane_k + (t & 1) * C::KSTAGE;
+        if constexpr (FP8) {
+            // e4m3: one 32x32x64 MFMA per 32 keys and 64 dims; a lane's 32 bytes of a K row
+            // (dims 64i + 32h ..) are two 16-byte reads
+            constexpr int NI = D / 64, NA = (BN / 32) * NI;
+            i32x8 a[NA];
+            const uint8_t* kf = smem + (t & 1) * C::KSTAGE + l32 * C::KROW + 32 * h;
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb) {
+                    const u32x4 a0 = ld16(kf + 32 * kb * C::KROW + 64 * i);
+                    const u32x4 a1 = ld16(kf + 32 * kb * C::KROW + 64 * i + 16);
+                    a[i * (BN / 32) + kb] = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                                  (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                }
+            f32x16 acc[BN / 32];
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) acc[kb] = f32x16{};
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const u32x4 b0 = qf[2 * i], b1 = qf[2 * i + 1];
+                const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb)   // e4m3 x e4m3, unit block scales (E8M0 127 = 2^0)
+                    acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i * (BN / 32) + kb], b, acc[kb], 0, 0, 0,
+                                                                              127, 0, 127);
+            }
+            pipeline_lds_mfma<NA, C::AHEAD / 2, 2>();
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) s[16 * kb + v] = acc[kb][v];
+            return;
+        }
         constexpr int NA = (BN / 32) * C::QREGS;
         bf16x8 a[NA];
 #pragma unroll
@@ -939,7 +1011,17 @@ void fwd_b128_kernel(KParams p) {
                 for (int v = 0; v < 16; ++v)
                     if (32 * kb + 8 * (v >> 2) + (v & 3) > lim) s[16 * kb + v] = kNegInf;   // acc_row(v, h) - 4h
         }
-        const float alpha = softmax_step(s, p.c_log2, m_run, l_run);
+        float alpha;
+        if constexpr (FP8) {
+            // 64-key halves carry their own K scales (64-row scale tiles); the second
+            // half of the last tile may lie past N (then its scale is never used)
+            const int ks = bh * n_scale + 2 * t;
+            const float c0 = c_q / p.k_scale[ks];
+            const float c1 = 2 * t + 1 < n_scale ? c_q / p.k_scale[ks + 1] : c0;
+            alpha = softmax_step2(s, c0, c1, m_run, l_run);
+        } else {
+            alpha = softmax_step(s, c_q, m_run, l_run);
+        }
         if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
@@ -1389,18 +1471,19 @@ __global__ __launch_bounds__(256) void quant_v_pow2_kernel(const uint8_t* __rest
 }
 
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool FP8>
 hipError_t launch_b128(KParams kp, int BH, hipStream_t st) {
-    kp.n_qtiles = (kp.N + B128Cfg::BM - 1) / B128Cfg::BM;
+    using C = B128Cfg<FP8>;
+    kp.n_qtiles = (kp.N + C::BM - 1) / C::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_b128_kernel<CAUSAL>), dim3(static_cast<int>(grid)), dim3(B128Cfg::NT), 0, st, kp);
+    hipLaunchKernelGGL((fwd_b128_kernel<CAUSAL, FP8>), dim3(static_cast<int>(grid)), dim3(C::NT), 0, st, kp);
     return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool FP8>
 hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
-    if constexpr (D == 128 && !FP8) return launch_b128<CAUSAL>(kp, BH, st);
+    if constexpr (D == 128) return launch_b128<CAUSAL, FP8>(kp, BH, st);
     kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
