@@ -127,8 +127,8 @@ def kernel_match(w) -> str:
     """Substring of the attention kernel's name in rocprofv3 output for a workload."""
     if w.dtype == "f32":
         return "fwd_f32_kernel"
-    if w.dtype == "bf16" and w.d == 128:
-        return f"fwd_b128_kernel<{'true' if w.causal else 'false'}>"
+    if w.dtype in ("bf16", "fp8") and w.d == 128:
+        return f"fwd_b128_kernel<{'true' if w.causal else 'false'}, {'true' if w.dtype == 'fp8' else 'false'}>"
     return f"fwd_pp_kernel<{w.d}, {'true' if w.causal else 'false'}, {'true' if w.dtype != 'bf16' else 'false'}, 0"
 
 
@@ -343,14 +343,15 @@ def bench_configs(flush_mib: int = 512):
     flush_buf = torch.empty(flush_mib << 20, dtype=torch.uint8, device="cuda")
     flush = lambda i: flush_buf.fill_(i & 0xFF)
     out = {}
-    for name, steps in (("c1_f32", 200), ("c2_bf16", 200), ("c2_bf16_causal", 200), ("c3_bf16", 20)):
+    # c3 runs 100 calls after 20 warm-up calls: with fewer, the clock is still settling under load
+    for name, steps, warm in (("c1_f32", 200, 5), ("c2_bf16", 200, 5), ("c2_bf16_causal", 200, 5), ("c3_bf16", 100, 20)):
         w = WORKLOADS[name]
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
         q, k, v = (torch.from_numpy(a).to("cuda").to(tdt) for a in make_inputs(w))
         o = torch.empty_like(q)
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
         call = lambda: fwd(q, k, v, causal=w.causal, dtype=w.dtype, out=o, lse=lse)
-        warm = _time_calls(call, steps, warmup=5)
+        warm = _time_calls(call, steps, warmup=warm)
         med = float(np.median(warm))
         r = {"shape": list(w.shape), "dtype": w.dtype, "causal": w.causal, "warm_ms": _stats(warm),
              "tflops": round(w.flops() / med / 1e9, 3),
