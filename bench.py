@@ -129,6 +129,8 @@ def kernel_match(w) -> str:
         return "fwd_f32_kernel"
     if w.dtype in ("bf16", "fp8") and w.d == 128:
         return f"fwd_b128_kernel<{'true' if w.causal else 'false'}, {'true' if w.dtype == 'fp8' else 'false'}>"
+    if w.dtype == "bf16" and w.d == 32:
+        return f"fwd_d32_kernel<{'true' if w.causal else 'false'}"
     return f"fwd_pp_kernel<{w.d}, {'true' if w.causal else 'false'}, {'true' if w.dtype != 'bf16' else 'false'}, 0"
 
 
@@ -250,6 +252,24 @@ def _time_calls(fn, steps: int, warmup: int = 3) -> np.ndarray:
     return np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
 
 
+def _time_back_to_back(fn, steps: int, warmup: int = 3) -> float:
+    """Mean ms per call of `steps` calls issued back to back between two events
+    (for calls of tens of microseconds the per-call events of _time_calls add
+    their own overhead to each call)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def bench_splitkv(w, steps: int):
     """fa_fwd vs fa_fwd_splitkv on the per-device share at eight devices (H/8 heads)."""
     import torch
@@ -323,12 +343,15 @@ def _time_cold(fn, steps: int, flush) -> np.ndarray:
     return np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
 
 
-# VALU floor for the small-d shapes: per score about four full-rate VALU
-# instructions (scale-and-subtract FMA, running sum, half a max3, half a
-# bf16 pack) at 2 cycles per wave64 instruction and one v_exp_f32 at about 6
-# (issue rates measured with a probe of independent chains), over 256 CUs x 4
-# SIMDs at 2.4 GHz.
-VALU_CYCLES_PER_SCORE = (4 * 2 + 6) / 64.0
+# VALU floor for the small-d shapes: per score one scale-and-subtract FMA, one
+# v_exp_f32, one add to the running sum and half a bf16 pack (the row max is
+# skipped while the reference holds), at 4 cycles per wave64 instruction on a
+# 16-lane SIMD and 8 for v_exp_f32: the d = 32 kernel's counters give
+# SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU = 1.23 quad-cycles per instruction, one
+# in four of them v_exp_f32, i.e. 1 quad-cycle per ordinary instruction and 2
+# per exp (profiles/fa_fwd_c2_bf16_valu_counters.md); over 256 CUs x 4 SIMDs
+# at 2.4 GHz.
+VALU_CYCLES_PER_SCORE = (4 + 8 + 4 + 2) / 64.0
 N_SIMD = 256 * 4
 CLOCK_HZ = 2.4e9
 
@@ -352,8 +375,9 @@ def bench_configs(flush_mib: int = 512):
         lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
         call = lambda: fwd(q, k, v, causal=w.causal, dtype=w.dtype, out=o, lse=lse)
         warm = _time_calls(call, steps, warmup=warm)
-        med = float(np.median(warm))
-        r = {"shape": list(w.shape), "dtype": w.dtype, "causal": w.causal, "warm_ms": _stats(warm),
+        med = _time_back_to_back(call, steps, warmup=5)
+        r = {"shape": list(w.shape), "dtype": w.dtype, "causal": w.causal,
+             "warm_ms_back_to_back": round(med, 5), "warm_ms": _stats(warm),
              "tflops": round(w.flops() / med / 1e9, 3),
              "pct_mfma_peak": round(100.0 * w.flops() / med / 1e9 / PEAK_TFLOPS[w.dtype], 2),
              "compulsory_bytes": w.compulsory_bytes()}

@@ -35,6 +35,19 @@ def test_small_shapes_full_output(gpu_lib, dtype, d, causal, N):
     compare(o, lse, o_ref, lse_ref, dtype, f"{dtype} d={d} causal={causal} N={N}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [300, 513, 777])
+def test_d32_stages_and_chunk_pairs(gpu_lib, causal, N):
+    """bf16 at d = 32 runs its tiles in 256-key stages through a two-stage ring and,
+    when causal, gives each workgroup a pair of 128-query chunks: these lengths wrap
+    the ring (N > 512) and leave an odd chunk count (one workgroup with a single
+    chunk), with ragged last stages."""
+    q, k, v = _small_inputs("bf16", 2, 2, N, 32, seed=3000 + N)
+    o, lse = gpu_forward(q, k, v, "bf16", causal, 0.2)
+    o_ref, lse_ref = oracle_forward(q, k, v, "bf16", causal, 0.2)
+    compare(o, lse, o_ref, lse_ref, "bf16", f"d=32 N={N} causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_ragged_long_tail(gpu_lib, dtype):
     q, k, v = _small_inputs(dtype, 1, 2, 1000, 64, seed=77)

@@ -94,6 +94,7 @@ enum : int { kModeDense = 0, kModePartial = 1, kModeSparse = 2 };
 // each new maximum would otherwise cost a rescale of the 64 O accumulators.
 // ---------------------------------------------------------------------------
 constexpr float kRescaleSlack = 45.0f;
+constexpr float kRescaleBound = 0x1p45f;     // 2^kRescaleSlack
 
 template <int NS>
 __device__ __forceinline__ float softmax_step(float (&s)[NS], float c, float& m, float& l) {
@@ -144,6 +145,33 @@ __device__ __forceinline__ float softmax_step2(float (&s)[NS], float c0, float c
     }
     l = fmaf(l, alpha, rs);
     return alpha;
+}
+
+// Probabilities against the current reference m alone, without the row max:
+// the first NS/2 scores scaled by c0, the rest by c1, packed to bf16 into pf,
+// their sum added to l.  Taken only when every lane's part of the sum is at
+// most 2^kRescaleSlack: then so is every probability, and softmax_step(2)
+// would have left the reference where it is and computed the same values in
+// the same order.  Otherwise (a new maximum far above the reference; an inf
+// or NaN score; m = -inf) it returns false for the whole wave and changes
+// nothing: the caller then takes the full step from the intact scores.
+template <int NS>
+__device__ __forceinline__ bool softmax_at_ref(const float (&s)[NS], float c0, float c1, float m, float& l,
+                                               bf16x8 (&pf)[NS / 8]) {
+    float rs = 0.0f;
+    float pr[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        pr[i] = fast_exp2(fmaf(s[i], i < NS / 2 ? c0 : c1, -m));
+        rs += pr[i];
+    }
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kRescaleBound)) != 0) return false;
+    l += rs;
+#pragma unroll
+    for (int cc = 0; cc < NS / 8; ++cc)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) pf[cc][t] = static_cast<__bf16>(pr[8 * cc + t]);
+    return true;
 }
 
 // Same step for an e4m3 P*V product: the probabilities come out multiplied by
@@ -253,9 +281,10 @@ struct PPCfg {
     static constexpr int QREGS = F8W ? D / 64 : D / 16;
 };
 
-// The dense d = 32 kernels ask for 128 VGPRs (four waves per SIMD: two
-// workgroups per CU); the others keep the wider budget, which they need (at
-// d = 64 the transposing V reads take the dense kernel past 128).
+// The dense d = 32 kernel (FP8; bf16 at d = 32 has a kernel of its own) asks
+// for 128 VGPRs (four waves per SIMD: two workgroups per CU); the others keep
+// the wider budget, which they need (at d = 64 the transposing V reads take
+// the dense kernel past 128).
 template <int D, bool CAUSAL, bool FP8, int MODE, bool PV8 = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((D == 32 && MODE == kModeDense) ? 4 : 2)))
 void fwd_pp_kernel(KParams p) {
@@ -1011,27 +1040,31 @@ void fwd_b128_kernel(KParams p) {
                 for (int v = 0; v < 16; ++v)
                     if (32 * kb + 8 * (v >> 2) + (v & 3) > lim) s[16 * kb + v] = kNegInf;   // acc_row(v, h) - 4h
         }
-        float alpha;
+        float c0 = c_q, c1 = c_q;
         if constexpr (FP8) {
             // 64-key halves carry their own K scales (64-row scale tiles); the second
             // half of the last tile may lie past N (then its scale is never used)
             const int ks = bh * n_scale + 2 * t;
-            const float c0 = c_q / p.k_scale[ks];
-            const float c1 = 2 * t + 1 < n_scale ? c_q / p.k_scale[ks + 1] : c0;
-            alpha = softmax_step2(s, c0, c1, m_run, l_run);
-        } else {
-            alpha = softmax_step(s, c_q, m_run, l_run);
+            c0 = c_q / p.k_scale[ks];
+            c1 = 2 * t + 1 < n_scale ? c_q / p.k_scale[ks + 1] : c0;
         }
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+        // FP8: past the first tile, the probabilities against the current reference
+        // first (softmax_at_ref), the full step only where that fails.  (Measured:
+        // FP8 +1-2 %; bf16 -0.3 % at 1x32x16384x128 causal, -1 % at 4x32x4096x128,
+        // so bf16 always takes the full step.)
+        if (!FP8 || t == 0 || !softmax_at_ref(s, c0, c1, m_run, l_run, pf)) {
+            const float alpha = FP8 ? softmax_step2(s, c0, c1, m_run, l_run) : softmax_step(s, c_q, m_run, l_run);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+                for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+            }
+#pragma unroll
+            for (int cc = 0; cc < BN / 16; ++cc)
+#pragma unroll
+                for (int t8 = 0; t8 < 8; ++t8) pf[cc][t8] = static_cast<__bf16>(s[8 * cc + t8]);
         }
-#pragma unroll
-        for (int cc = 0; cc < BN / 16; ++cc)
-#pragma unroll
-            for (int t8 = 0; t8 < 8; ++t8) pf[cc][t8] = static_cast<__bf16>(s[8 * cc + t8]);
     };
     auto masked_tile = [&](int t) { return (CAUSAL && t * BN + BN - 1 > qw0) || t * BN + BN > N; };
     // slot boundary: neither matrix-core nor vector work crosses it (left to
@@ -1125,6 +1158,219 @@ void fwd_b128_kernel(KParams p) {
                 for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(o[db][4 * g + e] * inv);
                 *reinterpret_cast<bf16x4*>(orow + 2 * (32 * db + 8 * g + 4 * h)) = out;
             }
+        if (p.lse != nullptr && h == 0)
+            p.lse[static_cast<size_t>(bh) * N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    }
+}
+
+// ===========================================================================
+// bf16, d = 32: every wave runs its own tiles, one barrier per 256 keys
+//
+// At d = 32 a 64-key tile is 8 MFMAs per wave against ~120 vector
+// instructions of softmax, so the vector ALUs bound the kernel, and a
+// ping-pong split (one group on the matrix cores while the other runs the
+// softmax, a barrier every 64 keys) leaves the copies too little time to land
+// and pays its barriers on short slots.  Here each wave computes S, the
+// softmax and P*V of a tile back to back, and the four waves a SIMD holds
+// (two workgroups per CU) overlap one another's matrix and vector work on
+// their own.  K and V arrive in stages of SK keys through a two-stage LDS-DMA
+// ring: at the one barrier per stage the next stage's copy is issued into the
+// buffer the last stage left, a whole stage of compute ahead of its use.
+//
+// Causal: workgroup i of a head takes the 128-query chunks i (waves 0-3) and
+// NC - 1 - i (waves 4-7) of its NC chunks, so every workgroup has the same
+// work, and so has every SIMD (one wave of each chunk).
+// ===========================================================================
+template <int SK_>
+struct D32Cfg {
+    static constexpr int D = 32, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 64;
+    static constexpr int SK = SK_;               // keys per stage
+    static constexpr int TPS = SK / BN;          // 64-key tiles per stage
+    static constexpr int KROW = D * 2 + 16;      // K row in LDS: 4 granules + 1 pad granule
+    static constexpr int VROW = D * 2;           // V row in LDS: natural, unpadded
+    static constexpr int KBYTES = SK * KROW, VBYTES = SK * VROW;
+    static constexpr int STAGE = KBYTES + VBYTES;
+    static constexpr int K_BLOCKS = KBYTES / 1024, BLOCKS = STAGE / 1024;
+    static constexpr int PER_W = (BLOCKS + NW - 1) / NW;
+    static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "LDS-DMA layout");
+};
+
+template <bool CAUSAL, int SK = 256, bool FAST = true>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void fwd_d32_kernel(KParams p) {
+    using C = D32Cfg<SK>;
+    constexpr int D = C::D, BN = C::BN, TPS = C::TPS;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    const int wi = blockIdx.x / p.BH;           // workgroup of the head
+    const int bh = blockIdx.x - wi * p.BH;
+    // this wave's 32 query rows start at qw0; the workgroup needs keys [0, kend)
+    int qw0, kend;
+    bool rows = true;
+    if (CAUSAL) {
+        const int nc = (N + 127) / 128, c_hi = nc - 1 - wi;
+        qw0 = 128 * (w < 4 ? wi : c_hi) + 32 * (w & 3);
+        rows = w < 4 || c_hi != wi;             // odd NC: the middle chunk has one set of waves
+        kend = min(N, 128 * c_hi + 128);
+    } else {
+        qw0 = C::BM * wi + 32 * w;
+        kend = N;
+    }
+    rows = rows && qw0 < N;
+    const int my_q = qw0 + l32;
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* qg = p.q + slice * 2;
+    const uint8_t* kg = p.k + slice * 2;
+    const uint8_t* vg = p.v + slice * 2;
+
+    const int n_st = (kend + SK - 1) / SK;
+    // tiles of this wave: keys [0, min(N, qw0 + 32)) when causal; a wave without
+    // rows only copies
+    const int n_t = !rows ? 0 : ((CAUSAL ? min(N, qw0 + 32) : N) + BN - 1) / BN;
+
+    // ---- stage copies: 1 KiB block b of a stage by wave b mod 8; K blocks hold
+    // padded rows (dma_lane_offset), V blocks the tile's bytes in order
+    const uint32_t smem_lds = lds_address(smem);
+    uint32_t off[C::PER_W];
+#pragma unroll
+    for (int i = 0; i < C::PER_W; ++i) {
+        const int b = w + C::NW * i;
+        off[i] = b < C::K_BLOCKS ? dma_lane_offset(b, lane, D * 2 / 16, D * 2, SK)
+                                 : static_cast<uint32_t>(1024 * (b - C::K_BLOCKS) + 16 * lane);
+    }
+    auto copy_stage = [&](int st) {
+        const int n0 = st * SK;
+        const uint32_t bytes = static_cast<uint32_t>(min(N - n0, SK) * D * 2);
+        const u32x4 kr = buffer_words(kg + static_cast<size_t>(n0) * D * 2, bytes);
+        const u32x4 vr = buffer_words(vg + static_cast<size_t>(n0) * D * 2, bytes);
+        const uint32_t base = smem_lds + (st & 1) * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::PER_W; ++i) {
+            const int b = w + C::NW * i;
+            if (b < C::BLOCKS) {
+                poison_block(base + 1024 * b);
+                lds_dma16(base + 1024 * b, b < C::K_BLOCKS ? kr : vr, off[i]);
+            }
+        }
+    };
+
+    f32x16 o = {};
+    float m_run = kNegInf, l_run = 0.0f;
+    float s[BN / 2];
+    bf16x8 pf[BN / 16];
+    u32x4 qf[2];
+
+    // V^T operand of O^T += V^T P^T: lane 16g + 4r + j reads dims 16(g & 1) + 4j ..
+    // of key row 16cc + 4(g >> 1) + r (+ 8) with the transposing read
+    uint32_t lane_vo;
+    {
+        const int g = lane >> 4, r = (lane >> 2) & 3, j = lane & 3;
+        lane_vo = (4 * (g >> 1) + r) * C::VROW + 16 * (2 * (g & 1) + (j >> 1)) + 8 * (j & 1);
+    }
+
+    // S^T = K Q^T for the tile at K row `kr0` of the stage whose lane address is kl
+    auto op_s = [&](const uint8_t* kl) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) a[2 * i + kb] = __builtin_bit_cast(bf16x8, ld16(kl + 32 * kb * C::KROW + 32 * i));
+        f32x16 acc[2] = {};
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                acc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * i + kb], __builtin_bit_cast(bf16x8, qf[i]), acc[kb],
+                                                                 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[16 * kb + v] = acc[kb][v];
+    };
+    bf16x8 va[4];                                 // V^T operand of the tile in flight
+    auto read_v = [&](const lds_u8* vb) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const i16x4 lo = ds_read_tr16(vb + 16 * cc * C::VROW);
+            const i16x4 hi = ds_read_tr16(vb + (16 * cc + 8) * C::VROW);
+            va[cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    auto op_pv = [&]() {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[cc], pf[cc], o, 0, 0, 0);
+    };
+    auto op_softmax = [&](int t) {
+        const int n0 = t * BN;
+        if ((CAUSAL && n0 + BN - 1 > qw0) || n0 + BN > N) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int key = n0 + 32 * kb + acc_row(v, h);
+                    if (key >= N || (CAUSAL && key > my_q)) s[16 * kb + v] = kNegInf;
+                }
+        }
+        if (FAST && t != 0 && softmax_at_ref(s, p.c_log2, p.c_log2, m_run, l_run, pf)) return;
+        const float alpha = softmax_step(s, p.c_log2, m_run, l_run);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[v] *= alpha;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int t8 = 0; t8 < 8; ++t8) pf[cc][t8] = static_cast<__bf16>(s[8 * cc + t8]);
+    };
+
+    copy_stage(0);
+    // Q fragments (B operand of S^T = K Q^T): dims 16i + 8h .. +7, loaded while
+    // the first stage is on its way and waited for here: a wait left to the loop
+    // (the compiler's vmcnt(0)) would also wait for the next stage's copies
+    {
+        const bool ok = my_q < N;
+        const uint8_t* row = qg + static_cast<size_t>(my_q) * D * 2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) qf[i] = ok ? ld16(row + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+        asm volatile("" : : "v"(qf[0]), "v"(qf[1]));
+    }
+    const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
+    const lds_u8* lane_v = (const lds_u8*)smem + C::KBYTES + lane_vo;
+    for (int st = 0; st < n_st; ++st) {
+        wait_lds_dma();                           // this wave's copies of stage st have landed
+        lds_barrier();                            // so have everyone's; stage st - 1 is read
+        if (st + 1 < n_st) copy_stage(st + 1);    // into the buffer stage st - 1 leaves
+        // per tile: the V reads go out before the softmax and the next tile's S
+        // after it, so that LDS and matrix-core latencies overlap this wave's
+        // own vector work
+        const int t0 = TPS * st, t1 = min(TPS * (st + 1), n_t);
+        const uint8_t* kl = lane_k + (st & 1) * C::STAGE;
+        const lds_u8* vl = lane_v + (st & 1) * C::STAGE;
+        if (t0 < t1) op_s(kl);
+        for (int t = t0; t < t1; ++t) {
+            read_v(vl + (t - t0) * BN * C::VROW);
+            op_softmax(t);
+            if (t + 1 < t1) op_s(kl + (t + 1 - t0) * BN * C::KROW);
+            op_pv();
+        }
+    }
+
+    // ---- epilogue
+    const float l_tot = sum_halves(l_run);
+    if (rows && my_q < N) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        uint8_t* orow = p.o + (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            bf16x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(o[4 * g + e] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 2 * (8 * g + 4 * h)) = out;
+        }
         if (p.lse != nullptr && h == 0)
             p.lse[static_cast<size_t>(bh) * N + my_q] = (m_run + __log2f(l_tot)) * kLn2;
     }
@@ -1481,15 +1727,31 @@ hipError_t launch_b128(KParams kp, int BH, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool FP8>
-hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
-    if constexpr (D == 128) return launch_b128<CAUSAL, FP8>(kp, BH, st);
-    kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
+template <bool CAUSAL>
+hipError_t launch_d32(KParams kp, int BH, hipStream_t st) {
+    using C = D32Cfg<256>;
+    // workgroups per head: 256-query tiles, or (causal) pairs of 128-query chunks
+    kp.n_qtiles = CAUSAL ? ((kp.N + 127) / 128 + 1) / 2 : (kp.N + C::BM - 1) / C::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8, kModeDense>), dim3(static_cast<int>(grid)),
-                       dim3(PPCfg<D, CAUSAL, FP8>::NT), 0, st, kp);
+    hipLaunchKernelGGL((fwd_d32_kernel<CAUSAL, 256>), dim3(static_cast<int>(grid)), dim3(C::NT), 0, st, kp);
     return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool FP8>
+hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
+    if constexpr (D == 128) {
+        return launch_b128<CAUSAL, FP8>(kp, BH, st);
+    } else if constexpr (D == 32 && !FP8) {
+        return launch_d32<CAUSAL>(kp, BH, st);
+    } else {
+        kp.n_qtiles = (kp.N + PPCfg<D, CAUSAL, FP8>::BM - 1) / PPCfg<D, CAUSAL, FP8>::BM;
+        const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
+        if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fwd_pp_kernel<D, CAUSAL, FP8, kModeDense>), dim3(static_cast<int>(grid)),
+                           dim3(PPCfg<D, CAUSAL, FP8>::NT), 0, st, kp);
+        return hipGetLastError();
+    }
 }
 template <int D, bool CAUSAL>
 hipError_t launch_fp8pv(KParams kp, int BH, hipStream_t st) {
