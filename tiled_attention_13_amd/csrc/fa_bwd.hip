@@ -14,6 +14,11 @@
 // synchronisation between thread blocks):
 //
 //  * bwd_prep_kernel: D_i and lse_i * log2(e) per query row.
+//  * At d = 128 the three kernels below run on the forward's ping-pong
+//    schedule instead (bwd_dq_pp_kernel, bwd_kv_pp_kernel): two wave groups
+//    one slot apart, so that one wave of each SIMD issues matrix-core work
+//    while the other runs the exp and dS arithmetic; the layouts and
+//    products are the same.
 //  * bwd_dq_kernel: query-stationary, the forward's layout.  A workgroup
 //    holds 256 queries (32 per wave, Q and dO in registers as MFMA B
 //    operands) and streams 64-key tiles of K, V and K^T through LDS;
@@ -267,6 +272,272 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
 }
 
 // ===========================================================================
+// dQ at d = 128 on the forward's ping-pong schedule.  Waves 0-3 (group A) and
+// 4-7 (group B) sit one per SIMD each and run one slot apart, so that each
+// SIMD holds one wave issuing matrix-core work while the other runs vector
+// work.  Per wave, for 32-key tiles t:
+//   M_t = { dQ^T += K_{t-1}^T dS_{t-1}^T,  S_t^T = K_t Q^T,  dP_t^T = V_t dO^T }
+//   V_t = { P = exp2(S c - lse2), dS^T = P (dP - D), packed to bf16 }
+// Group A runs op k in slot k, group B in slot k+1.  K and V rows of tile t
+// (one 20 KiB stage) are read in slots 2t and 2t+1, K^T of tile t (12 KiB) in
+// slots 2t+2 and 2t+3; group B copies KV_{j+2} and KT_{j+1} in its vector slot
+// 2j+2 into the stages the tiles two before left, and waits for them at the
+// end of slot 2j+3, before the barrier after which group A reads them.
+// ===========================================================================
+constexpr int kDqSlotKeys = 64;                          // keys per slot of the d = 128 dQ kernel
+template <int BN_>
+struct DqPPCfg {
+    static constexpr int D = 128, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = BN_;
+    static constexpr int KROW = 2 * D + 16;              // K / V row in LDS: 16 granules + 1 pad
+    static constexpr int TROW = 2 * BN + 16;             // K^T row in LDS: 4 granules + 1 pad
+    static constexpr int KREG = dma_region_bytes(BN * KROW);          // K, V: 9 KiB each (17 at BN = 64)
+    static constexpr int KV_BLOCKS = (2 * KREG / 1024 + 3) / 4 * 4;   // whole groups of four copy blocks
+    static constexpr int KT_BLOCKS = (D * TROW / 1024 + 3) / 4 * 4;
+    static constexpr int KVSTAGE = KV_BLOCKS * 1024, KTSTAGE = KT_BLOCKS * 1024;
+    static constexpr int SMEM = 2 * KVSTAGE + 2 * KTSTAGE;
+    static constexpr int QREGS = D / 16;
+    static constexpr int AHEAD = 6;
+};
+
+template <bool CAUSAL, int BN_>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_pp_kernel(BParams p) {
+    using C = DqPPCfg<BN_>;
+    constexpr int KB = BN_ / 32;                         // 32-key blocks per tile
+    constexpr int D = C::D, BM = C::BM, BN = C::BN;
+    static_assert(D * C::TROW % 1024 == 0, "LDS-DMA layout");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, grp = w >> 2, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    int qt = blockIdx.x / p.BH;
+    const int bh = blockIdx.x - qt * p.BH;
+    if (CAUSAL) qt = p.n_tiles - 1 - qt;                 // heaviest query tiles first
+    const int q0 = qt * BM, qw0 = q0 + 32 * w, my_q = qw0 + l32;
+
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* kg = p.k + slice * 2;
+    const uint8_t* vg = p.v + slice * 2;
+    const uint8_t* ktg = p.kt + static_cast<size_t>(bh) * D * p.np * 2;
+
+    // Q and dO rows of this lane's query (B operands), its lse2 and D
+    u32x4 qf[C::QREGS], gf[C::QREGS];
+    float lse2_q = 0.0f, d_q = 0.0f;
+    {
+        const bool ok = my_q < N;
+        const size_t off = (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i) {
+            qf[i] = ok ? ld16(p.q + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+            gf[i] = ok ? ld16(p.dout + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+        }
+        if (ok) {
+            lse2_q = p.lse2[static_cast<size_t>(bh) * N + my_q];
+            d_q = p.dsum[static_cast<size_t>(bh) * N + my_q];
+        }
+    }
+
+    const int n_all = (N + BN - 1) / BN;
+    const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
+    // last key tile with a key at or before this wave's last query
+    const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
+
+    // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i)
+    const uint32_t smem_lds = lds_address(smem);
+    const uint32_t kvbase = smem_lds, ktbase = smem_lds + 2 * C::KVSTAGE;
+    constexpr int KV_PER_W = C::KV_BLOCKS / 4, KT_PER_W = C::KT_BLOCKS / 4, KREG_BLOCKS = C::KREG / 1024;
+    uint32_t kv_off[KV_PER_W], kt_off[KT_PER_W];
+    if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < KV_PER_W; ++i) {
+            const int b = (w & 3) + 4 * i;            // K rows, then V rows, KREG_BLOCKS blocks each
+            kv_off[i] = dma_lane_offset(b % KREG_BLOCKS, lane, D / 8, D * 2, b < 2 * KREG_BLOCKS ? BN : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < KT_PER_W; ++i)
+            kt_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, BN / 8, p.np * 2, D);
+    }
+    auto copy_kv = [&](int t) {                     // K_t, V_t rows into KV stage t % 2
+        const int n0 = t * BN;
+        const uint32_t valid = static_cast<uint32_t>(min(N - n0, BN)) * D * 2;
+        const u32x4 kr = buffer_words(kg + static_cast<size_t>(n0) * D * 2, valid);
+        const u32x4 vr = buffer_words(vg + static_cast<size_t>(n0) * D * 2, valid);
+        const uint32_t st = kvbase + (t & 1) * C::KVSTAGE + 1024 * (w & 3);
+#pragma unroll
+        for (int i = 0; i < KV_PER_W; ++i) {
+            poison_block(st + 4096 * i);
+            lds_dma16(st + 4096 * i, (w & 3) + 4 * i < KREG_BLOCKS ? kr : vr, kv_off[i]);
+        }
+    };
+    auto copy_kt = [&](int t) {                     // K^T_t into KT stage t % 2
+        const int n0 = t * BN;
+        const u32x4 r = buffer_words(ktg + static_cast<size_t>(n0) * 2, (static_cast<uint32_t>(D) * p.np - n0) * 2);
+        const uint32_t st = ktbase + (t & 1) * C::KTSTAGE + 1024 * (w & 3);
+#pragma unroll
+        for (int i = 0; i < KT_PER_W; ++i) {
+            poison_block(st + 4096 * i);
+            lds_dma16(st + 4096 * i, r, kt_off[i]);
+        }
+    };
+
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+    f32x16 s[KB], dp[KB];
+    bf16x8 dsf[2 * KB];
+
+    // S^T and dP^T of tile t (32-key blocks kb)
+    auto op_s = [&](int t) {
+        const uint8_t* kr = smem + (t & 1) * C::KVSTAGE + l32 * C::KROW + 16 * h;
+        const uint8_t* vr = kr + C::KREG;
+        bf16x8 a[2 * KB * C::QREGS];
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                a[2 * (KB * i + kb)] = __builtin_bit_cast(bf16x8, ld16(kr + 32 * kb * C::KROW + 32 * i));
+                a[2 * (KB * i + kb) + 1] = __builtin_bit_cast(bf16x8, ld16(vr + 32 * kb * C::KROW + 32 * i));
+            }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            s[kb] = f32x16{};
+            dp[kb] = f32x16{};
+        }
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * (KB * i + kb)], __builtin_bit_cast(bf16x8, qf[i]),
+                                                               s[kb], 0, 0, 0);
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2 * (KB * i + kb) + 1],
+                                                                __builtin_bit_cast(bf16x8, gf[i]), dp[kb], 0, 0, 0);
+            }
+        pipeline_lds_mfma<2 * KB * C::QREGS, C::AHEAD>();
+    };
+    // dS^T of tile t (the key index of register v is t BN + acc_row(v, h))
+    auto op_v = [&](int t, bool masked) {
+        const int lim = min(N - 1, CAUSAL ? my_q : N - 1) - t * BN - 4 * h;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float ds[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float pr = fast_exp2(fmaf(s[kb][v], p.c_log2, -lse2_q));
+                if (masked && 32 * kb + 8 * (v >> 2) + (v & 3) > lim) pr = 0.0f;
+                ds[v] = pr * (dp[kb][v] - d_q);
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dsf[2 * kb + cc][e] = static_cast<__bf16>(ds[8 * cc + e]);
+        }
+    };
+    // dQ^T += K_t^T dS_t^T
+    auto op_dq = [&](int t) {
+        const uint8_t* tr = smem + 2 * C::KVSTAGE + (t & 1) * C::KTSTAGE + l32 * C::TROW + 16 * h;
+        constexpr int NC = 2 * KB;                      // 16-key chunks of the tile
+        bf16x8 a[NC * (D / 32)];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc)
+                a[NC * db + cc] = __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * cc));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc)
+                dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NC * db + cc], dsf[cc], dq[db], 0, 0, 0);
+        pipeline_lds_mfma<NC * (D / 32), C::AHEAD>();
+    };
+    auto masked_tile = [&](int t) { return (CAUSAL && t * BN + BN - 1 > qw0) || t * BN + BN > N; };
+    auto slot_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: group B copies KV_0 and waits; everyone meets at barrier 0
+    if (grp == 1) {
+        copy_kv(0);
+        wait_lds_dma();
+    }
+    lds_barrier();
+
+    const bool last_masked = masked_tile(j_last);
+    if (grp == 0) {
+        // A: M_0 | V_0 M_1 | ... | V_{n-1} M_n | idle
+        op_s(0);
+        slot_end();
+        for (int j = 0; j < j_last; ++j) {
+            op_v(j, false);
+            slot_end();
+            op_dq(j);
+            __builtin_amdgcn_sched_barrier(0);
+            op_s(j + 1);
+            slot_end();
+        }
+        op_v(j_last, last_masked);
+        slot_end();
+        op_dq(j_last);
+        slot_end();
+        for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: slots only
+            slot_end();
+            slot_end();
+        }
+        slot_end();
+    } else {
+        // B: copies | M_0 | V_0 + copies, M_1 | ... | V_{n-1} + copies, M_n
+        if (1 < n_kt) copy_kv(1);
+        copy_kt(0);
+        slot_end();
+        op_s(0);
+        wait_lds_dma();
+        slot_end();
+        auto copies = [&](int j) {
+            if (j + 2 < n_kt) copy_kv(j + 2);
+            if (j + 1 < n_kt) copy_kt(j + 1);
+        };
+        for (int j = 0; j < j_last; ++j) {
+            op_v(j, false);
+            copies(j);
+            slot_end();
+            op_dq(j);
+            __builtin_amdgcn_sched_barrier(0);
+            op_s(j + 1);
+            wait_lds_dma();
+            slot_end();
+        }
+        op_v(j_last, last_masked);
+        copies(j_last);
+        slot_end();
+        op_dq(j_last);
+        wait_lds_dma();
+        slot_end();
+        for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: copies for the others
+            copies(j);
+            slot_end();
+            wait_lds_dma();
+            slot_end();
+        }
+    }
+
+    if (my_q < N) {
+        uint8_t* orow = p.dq + (slice + static_cast<size_t>(my_q) * D) * 2;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 out;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(dq[db][4 * g + e] * p.scale);
+                *reinterpret_cast<bf16x4*>(orow + 2 * (32 * db + 8 * g + 4 * h)) = out;
+            }
+    }
+}
+
+// ===========================================================================
 // dV and dK as two key-stationary kernels of 8 waves x 32 keys (two waves per
 // SIMD, so one wave's softmax work overlaps the other's matrix-core work):
 //   WHICH = 0: S = Q K^T, P = exp2(S c - lse2), dV^T += dO^T P     (Q rows, dO^T, lse2 streamed)
@@ -477,6 +748,298 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
     }
 }
 
+// ===========================================================================
+// dV and dK at d = 128 on the forward's ping-pong schedule (key-stationary:
+// 8 waves x 32 keys, K and V rows in registers as B operands).  Per wave,
+// for BQ-query tiles t:
+//   M_t = { acc^T += X_{t-1}^T Y_{t-1},  S_t = Q_t K^T  (dK: and dP_t = dO_t V^T) }
+//   V_t = { P = exp2(S c - lse2)  (dK: dS = P (dP - D)), packed to bf16 }
+// with acc = dV, X = dO, Y = P, or acc = dK, X = Q, Y = dS.  Group A runs op k
+// in slot k, group B in slot k+1.  Stage t % 3 of the row ring holds Q_t (dK:
+// and dO_t) rows and the tile's lse2 (and D), read in slots 2t .. 2t+2; stage
+// t % 2 of the transposed ring holds dO_t^T (dK: Q_t^T), read in slots 2t+2
+// and 2t+3.  Group B copies R_{j+2} and T_{j+1} in its vector slot 2j+2 and
+// waits for them at the end of slot 2j+3.  Rows past the end of the sequence
+// read as zero (and so do their lse2 and D): their P is then 1, but every
+// product it enters has a zero factor (dO^T columns, dP and D).  A wave skips
+// the tiles whose queries all precede its keys (causal).
+// ===========================================================================
+constexpr int kDvSlotQueries = 64, kDkSlotQueries = 32;  // queries per slot of the d = 128 dV / dK kernels
+template <int WHICH, int BQ_>
+struct KvPPCfg {
+    static constexpr int D = 128, NW = 8, NT = 64 * NW, BK = 32 * NW, BQ = BQ_;
+    static constexpr int NR = WHICH == 0 ? 1 : 2;        // row tiles: Q (and dO)
+    static constexpr int NV = WHICH == 0 ? 1 : 2;        // row vectors: lse2 (and D), one 1 KiB block each
+    static constexpr int RROW = 2 * D + 16;
+    static constexpr int RREG = dma_region_bytes(BQ * RROW);
+    static constexpr int R_BLOCKS = (NR * RREG / 1024 + NV + 3) / 4 * 4;
+    static constexpr int TROW = 2 * BQ + 16;
+    static constexpr int T_BLOCKS = (D * TROW / 1024 + 3) / 4 * 4;
+    static constexpr int RSTAGE = R_BLOCKS * 1024, TSTAGE = T_BLOCKS * 1024;
+    static constexpr int SMEM = 3 * RSTAGE + 2 * TSTAGE;
+    static constexpr int QREGS = D / 16;
+    static constexpr int QB = BQ / 32;                   // 32-query blocks per tile
+    static constexpr int AHEAD = 6;
+};
+
+template <bool CAUSAL, int WHICH, int BQ_>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_kv_pp_kernel(BParams p) {
+    using C = KvPPCfg<WHICH, BQ_>;
+    constexpr int D = C::D, BK = C::BK, BQ = C::BQ, QB = C::QB, NR = C::NR;
+    static_assert(D * C::TROW % 1024 == 0, "LDS-DMA layout");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, grp = w >> 2, h = lane >> 5, l32 = lane & 31;
+    const int N = p.N;
+    const int kt = blockIdx.x / p.BH;                    // causal: low key tiles see the most queries
+    const int bh = blockIdx.x - kt * p.BH;
+    const int k0 = kt * BK, kw0 = k0 + 32 * w, my_k = kw0 + l32;
+
+    const size_t slice = static_cast<size_t>(bh) * N * D;
+    const uint8_t* qg = p.q + slice * 2;
+    const uint8_t* gg = p.dout + slice * 2;
+    const uint8_t* tg = (WHICH == 0 ? p.dot : p.qt) + static_cast<size_t>(bh) * D * p.np * 2;
+    const float* l2g = p.lse2 + static_cast<size_t>(bh) * N;
+    const float* dsg = p.dsum + static_cast<size_t>(bh) * N;
+
+    // K (and V) rows of this lane's key: B operands of S = Q K^T (and dP = dO V^T)
+    u32x4 kf[C::QREGS], vf[WHICH == 1 ? C::QREGS : 1];
+    {
+        const bool ok = my_k < N;
+        const size_t off = (slice + static_cast<size_t>(my_k) * D) * 2;
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i) {
+            kf[i] = ok ? ld16(p.k + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+            if constexpr (WHICH == 1) vf[i] = ok ? ld16(p.v + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
+        }
+    }
+
+    // query tiles [t0, t0 + n_t) of the workgroup; this wave's work starts at local tile j_first
+    const int n_qt = (N + BQ - 1) / BQ;
+    const int t0 = CAUSAL ? min(k0 / BQ, n_qt) : 0;
+    const int n_t = n_qt - t0;
+    const int j_first = CAUSAL ? min(n_t, kw0 / BQ - t0) : 0;
+
+    // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i)
+    const uint32_t smem_lds = lds_address(smem);
+    const uint32_t rbase = smem_lds, tbase = smem_lds + 3 * C::RSTAGE;
+    constexpr int R_PER_W = C::R_BLOCKS / 4, T_PER_W = C::T_BLOCKS / 4, RREG_BLOCKS = C::RREG / 1024;
+    uint32_t r_off[R_PER_W], t_off[T_PER_W];
+    if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < R_PER_W; ++i) {
+            const int b = (w & 3) + 4 * i;            // row tiles, then one block per row vector
+            if (b < NR * RREG_BLOCKS) r_off[i] = dma_lane_offset(b % RREG_BLOCKS, lane, D / 8, D * 2, BQ);
+            else r_off[i] = lane < BQ / 4 && b < NR * RREG_BLOCKS + C::NV ? 16u * lane : 0x40000000u;
+        }
+#pragma unroll
+        for (int i = 0; i < T_PER_W; ++i)
+            t_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, BQ / 8, p.np * 2, D);
+    }
+    auto copy_r = [&](int j) {                      // rows and vectors of tile t0 + j into R stage j % 3
+        const int m0 = (t0 + j) * BQ;
+        const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ));
+        const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
+        const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
+        const u32x4 rl = buffer_words(l2g + m0, valid * 4);
+        const u32x4 rd = buffer_words(dsg + m0, valid * 4);
+        const uint32_t st = rbase + (j % 3) * C::RSTAGE + 1024 * (w & 3);
+#pragma unroll
+        for (int i = 0; i < R_PER_W; ++i) {
+            const int b = (w & 3) + 4 * i;
+            poison_block(st + 4096 * i);
+            lds_dma16(st + 4096 * i,
+                      b < RREG_BLOCKS ? rq : b < NR * RREG_BLOCKS ? rg : b == NR * RREG_BLOCKS ? rl : rd, r_off[i]);
+        }
+    };
+    auto copy_t = [&](int j) {                      // transposed tile t0 + j into T stage j % 2
+        const int m0 = (t0 + j) * BQ;
+        const u32x4 r = buffer_words(tg + static_cast<size_t>(m0) * 2, (static_cast<uint32_t>(D) * p.np - m0) * 2);
+        const uint32_t st = tbase + (j & 1) * C::TSTAGE + 1024 * (w & 3);
+#pragma unroll
+        for (int i = 0; i < T_PER_W; ++i) {
+            poison_block(st + 4096 * i);
+            lds_dma16(st + 4096 * i, r, t_off[i]);
+        }
+    };
+
+    f32x16 acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    f32x16 s[QB], dp[WHICH == 1 ? QB : 1];
+    bf16x8 xf[2 * QB];
+
+    // S (and dP) of local tile j, 32-query blocks qb
+    auto op_s = [&](int j) {
+        const uint8_t* qr = smem + (j % 3) * C::RSTAGE + l32 * C::RROW + 16 * h;
+        constexpr int PER_I = NR * QB;
+        bf16x8 a[PER_I * C::QREGS];
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                a[PER_I * i + NR * qb] = __builtin_bit_cast(bf16x8, ld16(qr + 32 * qb * C::RROW + 32 * i));
+                if constexpr (WHICH == 1)
+                    a[PER_I * i + NR * qb + 1] = __builtin_bit_cast(bf16x8, ld16(qr + C::RREG + 32 * qb * C::RROW + 32 * i));
+            }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            s[qb] = f32x16{};
+            if constexpr (WHICH == 1) dp[qb] = f32x16{};
+        }
+#pragma unroll
+        for (int i = 0; i < C::QREGS; ++i)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PER_I * i + NR * qb], __builtin_bit_cast(bf16x8, kf[i]),
+                                                               s[qb], 0, 0, 0);
+                if constexpr (WHICH == 1)
+                    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PER_I * i + NR * qb + 1],
+                                                                    __builtin_bit_cast(bf16x8, vf[i]), dp[qb], 0, 0, 0);
+            }
+        pipeline_lds_mfma<PER_I * C::QREGS, C::AHEAD>();
+    };
+    // P (dK: dS) of local tile j; the query of register v of block qb is
+    // (t0 + j) BQ + 32 qb + acc_row(v, h)
+    auto op_v = [&](int j, bool masked) {
+        const float* l2s = reinterpret_cast<const float*>(smem + (j % 3) * C::RSTAGE + NR * C::RREG);
+        const float* dss = l2s + 256;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int rel = my_k - (t0 + j) * BQ - 32 * qb - 4 * h;   // masked when rel > 8*(v/4) + v%4
+            float x[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * qb + 8 * g + 4 * h);
+                f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (WHICH == 1) d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g + e;
+                    float pr = fast_exp2(fmaf(s[qb][v], p.c_log2, -l4[e]));
+                    if (masked && rel > 8 * g + e) pr = 0.0f;
+                    x[v] = WHICH == 0 ? pr : pr * (dp[qb][v] - d4[e]);
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[2 * qb + cc][e] = static_cast<__bf16>(x[8 * cc + e]);
+        }
+    };
+    // acc^T += X^T Y for local tile j
+    auto op_acc = [&](int j) {
+        const uint8_t* tr = smem + 3 * C::RSTAGE + (j & 1) * C::TSTAGE + l32 * C::TROW + 16 * h;
+        constexpr int NC = 2 * QB;                      // 16-query chunks of the tile
+        bf16x8 a[NC * (D / 32)];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc)
+                a[NC * db + cc] = __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * cc));
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc)
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NC * db + cc], xf[cc], acc[db], 0, 0, 0);
+        pipeline_lds_mfma<NC * (D / 32), C::AHEAD>();
+    };
+    // the first tile of the wave is the only one with queries before some of its keys
+    auto masked_tile = [&](int j) { return CAUSAL && (t0 + j) * BQ < kw0 + 31; };
+    auto slot_end = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: group B copies R_0 and waits; everyone meets at barrier 0
+    if (grp == 1 && n_t > 0) {
+        copy_r(0);
+        wait_lds_dma();
+    }
+    lds_barrier();
+
+    if (n_t > 0) {
+        if (grp == 0) {
+            // A: M_0 | V_0 M_1 | ... | V_{n-1} M_n | idle, from local tile j_first on
+            for (int j = 0; j < j_first; ++j) {       // queries all before this wave's keys: slots only
+                slot_end();
+                slot_end();
+            }
+            if (j_first < n_t) {
+                op_s(j_first);
+                slot_end();
+                op_v(j_first, masked_tile(j_first));
+                slot_end();
+                for (int j = j_first; j + 1 < n_t; ++j) {
+                    op_acc(j);
+                    __builtin_amdgcn_sched_barrier(0);
+                    op_s(j + 1);
+                    slot_end();
+                    op_v(j + 1, false);
+                    slot_end();
+                }
+                op_acc(n_t - 1);
+            }
+            slot_end();
+            slot_end();
+        } else {
+            // B: copies | M_0 | V_0 + copies, M_1 | ... | V_{n-1} + copies, M_n
+            auto copies = [&](int j) {
+                if (j + 2 < n_t) copy_r(j + 2);
+                if (j + 1 < n_t) copy_t(j + 1);
+            };
+            if (1 < n_t) copy_r(1);
+            copy_t(0);
+            slot_end();
+            for (int j = 0; j < j_first; ++j) {       // copies only
+                wait_lds_dma();
+                slot_end();
+                copies(j);
+                slot_end();
+            }
+            if (j_first < n_t) {
+                op_s(j_first);
+                wait_lds_dma();
+                slot_end();
+                op_v(j_first, masked_tile(j_first));
+                copies(j_first);
+                slot_end();
+                for (int j = j_first; j + 1 < n_t; ++j) {
+                    op_acc(j);
+                    __builtin_amdgcn_sched_barrier(0);
+                    op_s(j + 1);
+                    wait_lds_dma();
+                    slot_end();
+                    op_v(j + 1, false);
+                    copies(j + 1);
+                    slot_end();
+                }
+                op_acc(n_t - 1);
+            }
+            wait_lds_dma();
+            slot_end();
+        }
+    }
+
+    if (my_k < N) {
+        uint8_t* out = (WHICH == 0 ? p.dv : p.dk) + (slice + static_cast<size_t>(my_k) * D) * 2;
+        const float mul = WHICH == 0 ? 1.0f : p.scale;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(acc[db][4 * g + e] * mul);
+                *reinterpret_cast<bf16x4*>(out + 2 * (32 * db + 8 * g + 4 * h)) = ov;
+            }
+    }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(BParams bp, const void* o, const float* lse, float* lse2, float* dsum, hipStream_t st) {
     const long long rows = static_cast<long long>(bp.BH) * bp.N;
@@ -494,11 +1057,22 @@ hipError_t launch_bwd_d(BParams bp, const void* o, const float* lse, float* lse2
     b.n_tiles = (bp.N + KvCfg<D, 0>::BK - 1) / KvCfg<D, 0>::BK;
     const long long g2 = static_cast<long long>(b.n_tiles) * bp.BH;
     if (g1 > 0x7FFFFFFFLL || g2 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 0>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 0>::NT), 0, st, b);
+    if constexpr (D == 128) {
+        hipLaunchKernelGGL((bwd_kv_pp_kernel<CAUSAL, 0, kDvSlotQueries>), dim3(static_cast<int>(g2)), dim3(512), 0, st, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_kv_pp_kernel<CAUSAL, 1, kDkSlotQueries>), dim3(static_cast<int>(g2)), dim3(512), 0, st, b);
+    } else {
+        hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 0>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 0>::NT), 0, st, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 1>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 1>::NT), 0, st, b);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 1>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 1>::NT), 0, st, b);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<int>(g1)), dim3(DqCfg<D>::NT), 0, st, a);
+    if constexpr (D == 128) {
+        hipLaunchKernelGGL((bwd_dq_pp_kernel<CAUSAL, kDqSlotKeys>), dim3(static_cast<int>(g1)), dim3(DqPPCfg<kDqSlotKeys>::NT),
+                           0, st, a);
+    } else {
+        hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(static_cast<int>(g1)), dim3(DqCfg<D>::NT), 0, st, a);
+    }
     return hipGetLastError();
 }
 
