@@ -271,8 +271,9 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
  *   dQ = softmax_scale * dS K;  dK = softmax_scale * dS^T Q.
  * P and dS are rounded to bf16 for the matrix cores; accumulation is fp32.
  * The call allocates one stream-ordered workspace (hipMallocAsync /
- * hipFreeAsync on `stream`): Q, dO and K transposed (3*B*H*d*ceil(N/64)*64
- * bf16) and two float32 [B,H,N] row statistics.
+ * hipFreeAsync on `stream`): two float32 [B,H,N] row statistics and, for
+ * d = 32 and 64 only, Q, dO and K transposed (3*B*H*d*ceil(N/64)*64 bf16;
+ * at d = 128 the kernels read those operands out of the natural rows).
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv,

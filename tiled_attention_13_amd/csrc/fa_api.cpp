@@ -438,19 +438,25 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int BH = static_cast<int>(B * H), n = static_cast<int>(N), dd = static_cast<int>(d);
-    const size_t tb = round_up(vt_bytes(BH, n, dd), 256);
+    // d = 128 reads Q^T, dO^T and K^T out of natural rows (transposing LDS reads);
+    // d = 32 and 64 take transposed copies
+    const bool copies = dd != 128;
+    const size_t tb = copies ? round_up(vt_bytes(BH, n, dd), 256) : 0;
     const size_t vec = round_up(static_cast<size_t>(BH) * n * 4, 256);
     void* ws = nullptr;
     if ((st = ws_alloc(&ws, 3 * tb + 2 * vec, s)) != FA_OK) return st;
     uint8_t* base = static_cast<uint8_t*>(ws);
-    void* qt = base;
-    void* dot = base + tb;
-    void* kt = base + 2 * tb;
+    void* qt = copies ? base : nullptr;
+    void* dot = copies ? base + tb : nullptr;
+    void* kt = copies ? base + 2 * tb : nullptr;
     float* lse2 = reinterpret_cast<float*>(base + 3 * tb);
     float* dsum = reinterpret_cast<float*>(base + 3 * tb + vec);
-    hipError_t e = fa::launch_transpose_v(q, qt, BH, n, dd, s);
-    if (e == hipSuccess) e = fa::launch_transpose_v(dout, dot, BH, n, dd, s);
-    if (e == hipSuccess) e = fa::launch_transpose_v(k, kt, BH, n, dd, s);
+    hipError_t e = hipSuccess;
+    if (copies) {
+        e = fa::launch_transpose_v(q, qt, BH, n, dd, s);
+        if (e == hipSuccess) e = fa::launch_transpose_v(dout, dot, BH, n, dd, s);
+        if (e == hipSuccess) e = fa::launch_transpose_v(k, kt, BH, n, dd, s);
+    }
     if (e == hipSuccess) {
         fa::BwdArgs a{q, k, v, o, dout, lse, qt, dot, kt, lse2, dsum, dq, dk, dv,
                       BH, n, padded_keys(n), dd, causal == 1, softmax_scale};

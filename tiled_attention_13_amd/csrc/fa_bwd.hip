@@ -69,6 +69,32 @@ struct BParams {
     float scale;
 };
 
+// Natural-layout row tiles read with the transposing LDS read (d = 128): a
+// tile of R rows of 256 bytes, row r's 16-byte granule g at granule
+// tr_granule(r, g), an XOR and so its own inverse.  The transposing reads
+// take, per 32 lanes, four consecutive rows x 64 bytes; the swizzle puts
+// those four pieces on four distinct quarters of the 64 LDS banks.
+__device__ __forceinline__ int tr_granule(int row, int g) { return g ^ (4 * (row & 3)); }
+
+// Per-lane LDS-DMA source offset of the first of a wave's copy blocks of such
+// a tile: block (w & 3) + 4i holds rows 4 ((w & 3) + 4i) .. +3, so the blocks
+// of one wave are 16 rows (4 KiB of source) apart.
+__device__ __forceinline__ uint32_t tr_copy_offset(int w, int lane) {
+    const int row = 4 * (w & 3) + (lane >> 4);
+    return static_cast<uint32_t>(row * 256 + 16 * tr_granule(row, lane & 15));
+}
+
+// LDS byte offset, within such a tile, of the first transposing read of the
+// A operand X^T (32 head dims 32 db .. + 31, 16 rows of chunk 0) of
+// acc^T += X^T Y: lane 16g + 4r + j reads dims 32 db + 16 (g & 1) + 4j .. +3
+// of row 4 (g >> 1) + r; the second read of a chunk is 8 rows further on and
+// chunk cc is 16 cc rows further.  The eight rows a lane then holds are the
+// ones the MFMA's k-slots 8h .. 8h+7 meet in a score-layout Y fragment.
+__device__ __forceinline__ uint32_t tr_read_offset(int lane, int db) {
+    const int g = lane >> 4, r = (lane >> 2) & 3, j = lane & 3;
+    return (4 * (g >> 1) + r) * 256 + 64 * (db ^ r) + 16 * (2 * (g & 1) + (j >> 1)) + 8 * (j & 1);
+}
+
 // ===========================================================================
 // Pre-pass: D_i = sum_k dO_ik O_ik and lse_i * log2(e), one row per group of
 // D/8 lanes (16 bytes of O and dO per lane).
@@ -279,20 +305,20 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BParams p) {
 //   M_t = { dQ^T += K_{t-1}^T dS_{t-1}^T,  S_t^T = K_t Q^T,  dP_t^T = V_t dO^T }
 //   V_t = { P = exp2(S c - lse2), dS^T = P (dP - D), packed to bf16 }
 // Group A runs op k in slot k, group B in slot k+1.  K and V rows of tile t
-// (one 20 KiB stage) are read in slots 2t and 2t+1, K^T of tile t (12 KiB) in
-// slots 2t+2 and 2t+3; group B copies KV_{j+2} and KT_{j+1} in its vector slot
-// 2j+2 into the stages the tiles two before left, and waits for them at the
-// end of slot 2j+3, before the barrier after which group A reads them.
+// are read in slots 2t and 2t+1; the K rows of tile t again, in a second copy
+// read with the transposing LDS read (the K^T operand of dQ^T), in slots 2t+2
+// and 2t+3.  Group B copies KV_{j+2} and KT_{j+1} in its vector slot 2j+2 into
+// the stages the tiles two before left, and waits for them at the end of slot
+// 2j+3, before the barrier after which group A reads them.
 // ===========================================================================
 constexpr int kDqSlotKeys = 64;                          // keys per slot of the d = 128 dQ kernel
 template <int BN_>
 struct DqPPCfg {
     static constexpr int D = 128, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = BN_;
     static constexpr int KROW = 2 * D + 16;              // K / V row in LDS: 16 granules + 1 pad
-    static constexpr int TROW = 2 * BN + 16;             // K^T row in LDS: 4 granules + 1 pad
     static constexpr int KREG = dma_region_bytes(BN * KROW);          // K, V: 9 KiB each (17 at BN = 64)
     static constexpr int KV_BLOCKS = (2 * KREG / 1024 + 3) / 4 * 4;   // whole groups of four copy blocks
-    static constexpr int KT_BLOCKS = (D * TROW / 1024 + 3) / 4 * 4;
+    static constexpr int KT_BLOCKS = BN * 256 / 1024;                 // K rows, natural and swizzled
     static constexpr int KVSTAGE = KV_BLOCKS * 1024, KTSTAGE = KT_BLOCKS * 1024;
     static constexpr int SMEM = 2 * KVSTAGE + 2 * KTSTAGE;
     static constexpr int QREGS = D / 16;
@@ -305,7 +331,7 @@ void bwd_dq_pp_kernel(BParams p) {
     using C = DqPPCfg<BN_>;
     constexpr int KB = BN_ / 32;                         // 32-key blocks per tile
     constexpr int D = C::D, BM = C::BM, BN = C::BN;
-    static_assert(D * C::TROW % 1024 == 0, "LDS-DMA layout");
+    static_assert(C::KT_BLOCKS % 4 == 0, "LDS-DMA layout");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
 
     const int tid = threadIdx.x;
@@ -320,7 +346,6 @@ void bwd_dq_pp_kernel(BParams p) {
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* kg = p.k + slice * 2;
     const uint8_t* vg = p.v + slice * 2;
-    const uint8_t* ktg = p.kt + static_cast<size_t>(bh) * D * p.np * 2;
 
     // Q and dO rows of this lane's query (B operands), its lse2 and D
     u32x4 qf[C::QREGS], gf[C::QREGS];
@@ -343,21 +368,22 @@ void bwd_dq_pp_kernel(BParams p) {
     const int n_kt = CAUSAL ? min(n_all, (min(q0 + BM, N) + BN - 1) / BN) : n_all;
     // last key tile with a key at or before this wave's last query
     const int j_last = CAUSAL ? min(n_kt - 1, (qw0 + 31) / BN) : n_kt - 1;
+    uint32_t lane_to[D / 32];                       // transposing reads of the K^T operand
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) lane_to[db] = tr_read_offset(lane, db);
 
     // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i)
     const uint32_t smem_lds = lds_address(smem);
     const uint32_t kvbase = smem_lds, ktbase = smem_lds + 2 * C::KVSTAGE;
     constexpr int KV_PER_W = C::KV_BLOCKS / 4, KT_PER_W = C::KT_BLOCKS / 4, KREG_BLOCKS = C::KREG / 1024;
-    uint32_t kv_off[KV_PER_W], kt_off[KT_PER_W];
+    uint32_t kv_off[KV_PER_W], kt_off = 0;
     if (grp == 1) {
 #pragma unroll
         for (int i = 0; i < KV_PER_W; ++i) {
             const int b = (w & 3) + 4 * i;            // K rows, then V rows, KREG_BLOCKS blocks each
             kv_off[i] = dma_lane_offset(b % KREG_BLOCKS, lane, D / 8, D * 2, b < 2 * KREG_BLOCKS ? BN : 0);
         }
-#pragma unroll
-        for (int i = 0; i < KT_PER_W; ++i)
-            kt_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, BN / 8, p.np * 2, D);
+        kt_off = tr_copy_offset(w, lane);
     }
     auto copy_kv = [&](int t) {                     // K_t, V_t rows into KV stage t % 2
         const int n0 = t * BN;
@@ -371,14 +397,14 @@ void bwd_dq_pp_kernel(BParams p) {
             lds_dma16(st + 4096 * i, (w & 3) + 4 * i < KREG_BLOCKS ? kr : vr, kv_off[i]);
         }
     };
-    auto copy_kt = [&](int t) {                     // K^T_t into KT stage t % 2
+    auto copy_kt = [&](int t) {                     // K_t rows, swizzled, into KT stage t % 2
         const int n0 = t * BN;
-        const u32x4 r = buffer_words(ktg + static_cast<size_t>(n0) * 2, (static_cast<uint32_t>(D) * p.np - n0) * 2);
+        const u32x4 r = buffer_words(kg + static_cast<size_t>(n0) * D * 2, static_cast<uint32_t>(min(N - n0, BN)) * D * 2);
         const uint32_t st = ktbase + (t & 1) * C::KTSTAGE + 1024 * (w & 3);
 #pragma unroll
         for (int i = 0; i < KT_PER_W; ++i) {
             poison_block(st + 4096 * i);
-            lds_dma16(st + 4096 * i, r, kt_off[i]);
+            lds_dma16(st + 4096 * i, r, kt_off + 4096 * i);
         }
     };
 
@@ -436,20 +462,23 @@ void bwd_dq_pp_kernel(BParams p) {
     };
     // dQ^T += K_t^T dS_t^T
     auto op_dq = [&](int t) {
-        const uint8_t* tr = smem + 2 * C::KVSTAGE + (t & 1) * C::KTSTAGE + l32 * C::TROW + 16 * h;
+        const lds_u8* ts = (const lds_u8*)smem + 2 * C::KVSTAGE + (t & 1) * C::KTSTAGE;
         constexpr int NC = 2 * KB;                      // 16-key chunks of the tile
         bf16x8 a[NC * (D / 32)];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int cc = 0; cc < NC; ++cc)
-                a[NC * db + cc] = __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * cc));
+            for (int cc = 0; cc < NC; ++cc) {
+                const i16x4 lo = ds_read_tr16(ts + lane_to[db] + 16 * cc * 256);
+                const i16x4 hi = ds_read_tr16(ts + lane_to[db] + (16 * cc + 8) * 256);
+                a[NC * db + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc)
                 dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NC * db + cc], dsf[cc], dq[db], 0, 0, 0);
-        pipeline_lds_mfma<NC * (D / 32), C::AHEAD>();
+        pipeline_lds_mfma<NC * (D / 32), C::AHEAD, 2>();
     };
     auto masked_tile = [&](int t) { return (CAUSAL && t * BN + BN - 1 > qw0) || t * BN + BN > N; };
     auto slot_end = [&]() {
@@ -755,16 +784,17 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
 //   M_t = { acc^T += X_{t-1}^T Y_{t-1},  S_t = Q_t K^T  (dK: and dP_t = dO_t V^T) }
 //   V_t = { P = exp2(S c - lse2)  (dK: dS = P (dP - D)), packed to bf16 }
 // with acc = dV, X = dO, Y = P, or acc = dK, X = Q, Y = dS.  Group A runs op k
-// in slot k, group B in slot k+1.  Stage t % 3 of the row ring holds Q_t (dK:
-// and dO_t) rows and the tile's lse2 (and D), read in slots 2t .. 2t+2; stage
-// t % 2 of the transposed ring holds dO_t^T (dK: Q_t^T), read in slots 2t+2
-// and 2t+3.  Group B copies R_{j+2} and T_{j+1} in its vector slot 2j+2 and
-// waits for them at the end of slot 2j+3.  Rows past the end of the sequence
-// read as zero (and so do their lse2 and D): their P is then 1, but every
-// product it enters has a zero factor (dO^T columns, dP and D).  A wave skips
-// the tiles whose queries all precede its keys (causal).
+// in slot k, group B in slot k+1.  Stage t % 2 of the row ring holds Q_t (dK:
+// and dO_t) rows, read in slots 2t and 2t+1; stage t % 3 of the vector ring the
+// tile's lse2 (and D), read in slots 2t+1 and 2t+2; stage t % 2 of the
+// transposed ring dO_t (dK: Q_t) rows again, natural and swizzled, read with
+// the transposing LDS read as dO_t^T (Q_t^T) in slots 2t+2 and 2t+3.  Group B
+// copies R_{j+2}, L_{j+2} and T_{j+1} in its vector slot 2j+2 and waits for
+// them at the end of slot 2j+3.  Rows past the end of the sequence read as
+// zero (and so do their lse2 and D) and get P = 0.  A wave skips the tiles
+// whose queries all precede its keys (causal).
 // ===========================================================================
-constexpr int kDvSlotQueries = 64, kDkSlotQueries = 32;  // queries per slot of the d = 128 dV / dK kernels
+constexpr int kDvSlotQueries = 64, kDkSlotQueries = 32;   // queries per slot of the d = 128 dV / dK kernels
 template <int WHICH, int BQ_>
 struct KvPPCfg {
     static constexpr int D = 128, NW = 8, NT = 64 * NW, BK = 32 * NW, BQ = BQ_;
@@ -772,11 +802,10 @@ struct KvPPCfg {
     static constexpr int NV = WHICH == 0 ? 1 : 2;        // row vectors: lse2 (and D), one 1 KiB block each
     static constexpr int RROW = 2 * D + 16;
     static constexpr int RREG = dma_region_bytes(BQ * RROW);
-    static constexpr int R_BLOCKS = (NR * RREG / 1024 + NV + 3) / 4 * 4;
-    static constexpr int TROW = 2 * BQ + 16;
-    static constexpr int T_BLOCKS = (D * TROW / 1024 + 3) / 4 * 4;
-    static constexpr int RSTAGE = R_BLOCKS * 1024, TSTAGE = T_BLOCKS * 1024;
-    static constexpr int SMEM = 3 * RSTAGE + 2 * TSTAGE;
+    static constexpr int R_BLOCKS = (NR * RREG / 1024 + 3) / 4 * 4;
+    static constexpr int T_BLOCKS = BQ * 256 / 1024;    // natural, swizzled rows
+    static constexpr int RSTAGE = R_BLOCKS * 1024, TSTAGE = T_BLOCKS * 1024, LSTAGE = NV * 1024;
+    static constexpr int SMEM = 2 * RSTAGE + 2 * TSTAGE + 3 * LSTAGE;
     static constexpr int QREGS = D / 16;
     static constexpr int QB = BQ / 32;                   // 32-query blocks per tile
     static constexpr int AHEAD = 6;
@@ -787,7 +816,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kv_pp_kernel(BParams p) {
     using C = KvPPCfg<WHICH, BQ_>;
     constexpr int D = C::D, BK = C::BK, BQ = C::BQ, QB = C::QB, NR = C::NR;
-    static_assert(D * C::TROW % 1024 == 0, "LDS-DMA layout");
+    static_assert(C::T_BLOCKS % 4 == 0, "LDS-DMA layout");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
 
     const int tid = threadIdx.x;
@@ -801,7 +830,7 @@ void bwd_kv_pp_kernel(BParams p) {
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* qg = p.q + slice * 2;
     const uint8_t* gg = p.dout + slice * 2;
-    const uint8_t* tg = (WHICH == 0 ? p.dot : p.qt) + static_cast<size_t>(bh) * D * p.np * 2;
+    const uint8_t* tg = WHICH == 0 ? gg : qg;            // rows of the transposed operand
     const float* l2g = p.lse2 + static_cast<size_t>(bh) * N;
     const float* dsg = p.dsum + static_cast<size_t>(bh) * N;
 
@@ -825,44 +854,44 @@ void bwd_kv_pp_kernel(BParams p) {
 
     // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i)
     const uint32_t smem_lds = lds_address(smem);
-    const uint32_t rbase = smem_lds, tbase = smem_lds + 3 * C::RSTAGE;
+    const uint32_t rbase = smem_lds, tbase = smem_lds + 2 * C::RSTAGE, lbase = tbase + 2 * C::TSTAGE;
     constexpr int R_PER_W = C::R_BLOCKS / 4, T_PER_W = C::T_BLOCKS / 4, RREG_BLOCKS = C::RREG / 1024;
-    uint32_t r_off[R_PER_W], t_off[T_PER_W];
+    uint32_t r_off[R_PER_W], t_off = 0;
     if (grp == 1) {
 #pragma unroll
         for (int i = 0; i < R_PER_W; ++i) {
-            const int b = (w & 3) + 4 * i;            // row tiles, then one block per row vector
-            if (b < NR * RREG_BLOCKS) r_off[i] = dma_lane_offset(b % RREG_BLOCKS, lane, D / 8, D * 2, BQ);
-            else r_off[i] = lane < BQ / 4 && b < NR * RREG_BLOCKS + C::NV ? 16u * lane : 0x40000000u;
+            const int b = (w & 3) + 4 * i;            // Q rows, then dO rows
+            r_off[i] = dma_lane_offset(b % RREG_BLOCKS, lane, D / 8, D * 2, b < NR * RREG_BLOCKS ? BQ : 0);
         }
-#pragma unroll
-        for (int i = 0; i < T_PER_W; ++i)
-            t_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, BQ / 8, p.np * 2, D);
+        t_off = tr_copy_offset(w, lane);
     }
-    auto copy_r = [&](int j) {                      // rows and vectors of tile t0 + j into R stage j % 3
-        const int m0 = (t0 + j) * BQ;
+    auto copy_r = [&](int j) {                      // rows of tile t0 + j into R stage j % 2, its
+        const int m0 = (t0 + j) * BQ;                // lse2 (and D) into L stage j % 3
         const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ));
         const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
         const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
-        const u32x4 rl = buffer_words(l2g + m0, valid * 4);
-        const u32x4 rd = buffer_words(dsg + m0, valid * 4);
-        const uint32_t st = rbase + (j % 3) * C::RSTAGE + 1024 * (w & 3);
+        const uint32_t st = rbase + (j & 1) * C::RSTAGE + 1024 * (w & 3);
 #pragma unroll
         for (int i = 0; i < R_PER_W; ++i) {
             const int b = (w & 3) + 4 * i;
             poison_block(st + 4096 * i);
-            lds_dma16(st + 4096 * i,
-                      b < RREG_BLOCKS ? rq : b < NR * RREG_BLOCKS ? rg : b == NR * RREG_BLOCKS ? rl : rd, r_off[i]);
+            lds_dma16(st + 4096 * i, b < RREG_BLOCKS ? rq : rg, r_off[i]);
+        }
+        if ((w & 3) < C::NV) {                       // one block per vector, by the first NV copying waves
+            const u32x4 rv = buffer_words((w & 3) == 0 ? l2g + m0 : dsg + m0, valid * 4);
+            const uint32_t lb = lbase + (j % 3) * C::LSTAGE + 1024 * (w & 3);
+            poison_block(lb);
+            lds_dma16(lb, rv, lane < BQ / 4 ? 16u * lane : 0x40000000u);
         }
     };
-    auto copy_t = [&](int j) {                      // transposed tile t0 + j into T stage j % 2
+    auto copy_t = [&](int j) {                      // rows of tile t0 + j, swizzled, into T stage j % 2
         const int m0 = (t0 + j) * BQ;
-        const u32x4 r = buffer_words(tg + static_cast<size_t>(m0) * 2, (static_cast<uint32_t>(D) * p.np - m0) * 2);
+        const u32x4 r = buffer_words(tg + static_cast<size_t>(m0) * D * 2, static_cast<uint32_t>(min(N - m0, BQ)) * D * 2);
         const uint32_t st = tbase + (j & 1) * C::TSTAGE + 1024 * (w & 3);
 #pragma unroll
         for (int i = 0; i < T_PER_W; ++i) {
             poison_block(st + 4096 * i);
-            lds_dma16(st + 4096 * i, r, t_off[i]);
+            lds_dma16(st + 4096 * i, r, t_off + 4096 * i);
         }
     };
 
@@ -870,11 +899,14 @@ void bwd_kv_pp_kernel(BParams p) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     f32x16 s[QB], dp[WHICH == 1 ? QB : 1];
+    uint32_t lane_to[D / 32];                       // transposing reads of the X^T operand
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) lane_to[db] = tr_read_offset(lane, db);
     bf16x8 xf[2 * QB];
 
     // S (and dP) of local tile j, 32-query blocks qb
     auto op_s = [&](int j) {
-        const uint8_t* qr = smem + (j % 3) * C::RSTAGE + l32 * C::RROW + 16 * h;
+        const uint8_t* qr = smem + (j & 1) * C::RSTAGE + l32 * C::RROW + 16 * h;
         constexpr int PER_I = NR * QB;
         bf16x8 a[PER_I * C::QREGS];
 #pragma unroll
@@ -903,13 +935,17 @@ void bwd_kv_pp_kernel(BParams p) {
         pipeline_lds_mfma<PER_I * C::QREGS, C::AHEAD>();
     };
     // P (dK: dS) of local tile j; the query of register v of block qb is
-    // (t0 + j) BQ + 32 qb + acc_row(v, h)
-    auto op_v = [&](int j, bool masked) {
-        const float* l2s = reinterpret_cast<const float*>(smem + (j % 3) * C::RSTAGE + NR * C::RREG);
+    // (t0 + j) BQ + 32 qb + acc_row(v, h).  masked: causal, queries before the
+    // key get P = 0; ragged: the tile ends past N, whose queries get P = 0 (a
+    // BQ-query tile may end past the K^T / dO^T padding, which is only rounded
+    // up to 64 keys, and read the next row there)
+    auto op_v = [&](int j, bool masked, bool ragged) {
+        const float* l2s = reinterpret_cast<const float*>(smem + 2 * C::RSTAGE + 2 * C::TSTAGE + (j % 3) * C::LSTAGE);
         const float* dss = l2s + 256;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int rel = my_k - (t0 + j) * BQ - 32 * qb - 4 * h;   // masked when rel > 8*(v/4) + v%4
+            const int lim = N - 1 - ((t0 + j) * BQ + 32 * qb + 4 * h);  // ragged: past N when 8*(v/4) + v%4 > lim
             float x[16];
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
@@ -920,7 +956,7 @@ void bwd_kv_pp_kernel(BParams p) {
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
                     float pr = fast_exp2(fmaf(s[qb][v], p.c_log2, -l4[e]));
-                    if (masked && rel > 8 * g + e) pr = 0.0f;
+                    if ((masked && rel > 8 * g + e) || (ragged && 8 * g + e > lim)) pr = 0.0f;
                     x[v] = WHICH == 0 ? pr : pr * (dp[qb][v] - d4[e]);
                 }
             }
@@ -932,23 +968,28 @@ void bwd_kv_pp_kernel(BParams p) {
     };
     // acc^T += X^T Y for local tile j
     auto op_acc = [&](int j) {
-        const uint8_t* tr = smem + 3 * C::RSTAGE + (j & 1) * C::TSTAGE + l32 * C::TROW + 16 * h;
+        const lds_u8* ts = (const lds_u8*)smem + 2 * C::RSTAGE + (j & 1) * C::TSTAGE;
         constexpr int NC = 2 * QB;                      // 16-query chunks of the tile
         bf16x8 a[NC * (D / 32)];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int cc = 0; cc < NC; ++cc)
-                a[NC * db + cc] = __builtin_bit_cast(bf16x8, ld16(tr + 32 * db * C::TROW + 32 * cc));
+            for (int cc = 0; cc < NC; ++cc) {
+                const i16x4 lo = ds_read_tr16(ts + lane_to[db] + 16 * cc * 256);
+                const i16x4 hi = ds_read_tr16(ts + lane_to[db] + (16 * cc + 8) * 256);
+                a[NC * db + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc)
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NC * db + cc], xf[cc], acc[db], 0, 0, 0);
-        pipeline_lds_mfma<NC * (D / 32), C::AHEAD>();
+        pipeline_lds_mfma<NC * (D / 32), C::AHEAD, 2>();
     };
-    // the first tile of the wave is the only one with queries before some of its keys
+    // the first tile of the wave is the only one with queries before some of its
+    // keys; the last may end past N
     auto masked_tile = [&](int j) { return CAUSAL && (t0 + j) * BQ < kw0 + 31; };
+    auto ragged_tile = [&](int j) { return (t0 + j) * BQ + BQ > N; };
     auto slot_end = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
@@ -972,14 +1013,14 @@ void bwd_kv_pp_kernel(BParams p) {
             if (j_first < n_t) {
                 op_s(j_first);
                 slot_end();
-                op_v(j_first, masked_tile(j_first));
+                op_v(j_first, masked_tile(j_first), ragged_tile(j_first));
                 slot_end();
                 for (int j = j_first; j + 1 < n_t; ++j) {
                     op_acc(j);
                     __builtin_amdgcn_sched_barrier(0);
                     op_s(j + 1);
                     slot_end();
-                    op_v(j + 1, false);
+                    op_v(j + 1, false, ragged_tile(j + 1));
                     slot_end();
                 }
                 op_acc(n_t - 1);
@@ -1005,7 +1046,7 @@ void bwd_kv_pp_kernel(BParams p) {
                 op_s(j_first);
                 wait_lds_dma();
                 slot_end();
-                op_v(j_first, masked_tile(j_first));
+                op_v(j_first, masked_tile(j_first), ragged_tile(j_first));
                 copies(j_first);
                 slot_end();
                 for (int j = j_first; j + 1 < n_t; ++j) {
@@ -1014,7 +1055,7 @@ void bwd_kv_pp_kernel(BParams p) {
                     op_s(j + 1);
                     wait_lds_dma();
                     slot_end();
-                    op_v(j + 1, false);
+                    op_v(j + 1, false, ragged_tile(j + 1));
                     copies(j + 1);
                     slot_end();
                 }
