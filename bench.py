@@ -469,7 +469,8 @@ def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
             "flop_convention": "2.5 x forward FLOPs (dV, dP, dQ, dK plus the recomputed S)",
             "mfma_tflops_executed": round(executed / (ms * 1e-3) / 1e12, 2),
             "pct_mfma_peak": round(100.0 * executed / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2),
-            "kernels": "bwd_prep_kernel, 3 x transpose_v_kernel, bwd_kv_kernel (dV), bwd_kv_kernel (dK), bwd_dq_kernel"}
+            "kernels": "bwd_prep_kernel, bwd_kv_pp_kernel (dV, 64-query slots), bwd_kv_pp_kernel (dK, 32-query "
+                       "slots), bwd_dq_pp_kernel (64-key slots); no transposition pre-pass at d = 128"}
 
 
 def _cpu_model() -> str:
