@@ -463,14 +463,14 @@ def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
     per_call = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
     ms = float(per_call.mean())
     conv = 2.5 * w.flops()
-    executed = 4.0 * w.flops()     # S three times (dV, dK, dQ kernels), dP twice, dV, dK, dQ once
+    executed = 3.5 * w.flops()     # d = 128: S twice (dK/dV, dQ kernels), dP twice, dV, dK, dQ once
     return {"ms_per_call": round(ms, 4), "median_ms": round(float(np.median(per_call)), 4),
             "tflops": round(conv / (ms * 1e-3) / 1e12, 2),
             "flop_convention": "2.5 x forward FLOPs (dV, dP, dQ, dK plus the recomputed S)",
             "mfma_tflops_executed": round(executed / (ms * 1e-3) / 1e12, 2),
             "pct_mfma_peak": round(100.0 * executed / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 2),
-            "kernels": "bwd_prep_kernel, bwd_kv_pp_kernel (dV, 64-query slots), bwd_kv_pp_kernel (dK, 32-query "
-                       "slots), bwd_dq_pp_kernel (64-key slots); no transposition pre-pass at d = 128"}
+            "kernels": "bwd_prep_kernel, bwd_kvf_kernel (dK and dV, S once, 64-query slots), bwd_dq_pp_kernel "
+                       "(64-key slots); no transposition pre-pass at d = 128"}
 
 
 def _cpu_model() -> str:

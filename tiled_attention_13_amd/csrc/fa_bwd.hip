@@ -14,11 +14,11 @@
 // synchronisation between thread blocks):
 //
 //  * bwd_prep_kernel: D_i and lse_i * log2(e) per query row.
-//  * At d = 128 the three kernels below run on the forward's ping-pong
-//    schedule instead (bwd_dq_pp_kernel, bwd_kv_pp_kernel): two wave groups
-//    one slot apart, so that one wave of each SIMD issues matrix-core work
-//    while the other runs the exp and dS arithmetic; the layouts and
-//    products are the same.
+//  * At d = 128 two kernels on the forward's ping-pong schedule replace the
+//    three below (bwd_dq_pp_kernel for dQ; bwd_kvf_kernel for dK and dV
+//    together, S computed once): two wave groups one slot apart, so that one
+//    wave of each SIMD issues matrix-core work while the other runs the exp
+//    and dS arithmetic.
 //  * bwd_dq_kernel: query-stationary, the forward's layout.  A workgroup
 //    holds 256 queries (32 per wave, Q and dO in registers as MFMA B
 //    operands) and streams 64-key tiles of K, V and K^T through LDS;
@@ -778,45 +778,44 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
 }
 
 // ===========================================================================
-// dV and dK at d = 128 on the forward's ping-pong schedule (key-stationary:
-// 8 waves x 32 keys, K and V rows in registers as B operands).  Per wave,
-// for BQ-query tiles t:
-//   M_t = { acc^T += X_{t-1}^T Y_{t-1},  S_t = Q_t K^T  (dK: and dP_t = dO_t V^T) }
-//   V_t = { P = exp2(S c - lse2)  (dK: dS = P (dP - D)), packed to bf16 }
-// with acc = dV, X = dO, Y = P, or acc = dK, X = Q, Y = dS.  Group A runs op k
-// in slot k, group B in slot k+1.  Stage t % 2 of the row ring holds Q_t (dK:
-// and dO_t) rows, read in slots 2t and 2t+1; stage t % 3 of the vector ring the
-// tile's lse2 (and D), read in slots 2t+1 and 2t+2; stage t % 2 of the
-// transposed ring dO_t (dK: Q_t) rows again, natural and swizzled, read with
-// the transposing LDS read as dO_t^T (Q_t^T) in slots 2t+2 and 2t+3.  Group B
-// copies R_{j+2}, L_{j+2} and T_{j+1} in its vector slot 2j+2 and waits for
-// them at the end of slot 2j+3.  Rows past the end of the sequence read as
-// zero (and so do their lse2 and D) and get P = 0.  A wave skips the tiles
-// whose queries all precede its keys (causal).
+// dK and dV of d = 128 in one kernel, S computed once: the 8 waves form four
+// pairs (w, w + 4) on one SIMD sharing 32 keys.  Wave w (group A) holds K and
+// accumulates dV, wave w + 4 (group B) holds V and accumulates dK; they run
+// the ping-pong one slot apart, so each SIMD holds one wave on its matrix
+// cores while the other runs vector work.  Per 64-query tile t:
+//   A: M_t = { dV^T += dO_{t-1}^T P_{t-1},  S_t = Q_t K^T }
+//      V_t = { P_t = exp2(S c - lse2) (masked), to bf16, handed to B through LDS }
+//   B: M_t = { dK^T += Q_{t-1}^T dS_{t-1},  dP_t = dO_t V^T }
+//      V_t = { dS_t = P_t (dP - D) from A's bf16 P, to bf16 }
+// A runs op k in slot k, B in slot k+1, so P_t is written in slot 2t+1 and
+// read in slot 2t+2.  Row ring (2 stages): Q and dO rows, read in slots 2t,
+// 2t+1; transposed ring (2 stages): dO and Q rows again, natural and swizzled,
+// read with the transposing LDS read in slots 2t+2, 2t+3; vector ring (3
+// stages): lse2 and D, read in slots 2t+1, 2t+2.  Group B copies R_{j+2},
+// L_{j+2} and T_{j+1} in its vector slot 2j+2 and waits for them at the end of
+// slot 2j+3.  Against the split dV and dK kernels this saves the dV kernel's
+// S; dS is formed from the bf16 P (the value P*V sees) instead of the fp32 one.
 // ===========================================================================
-constexpr int kDvSlotQueries = 64, kDkSlotQueries = 32;   // queries per slot of the d = 128 dV / dK kernels
-template <int WHICH, int BQ_>
-struct KvPPCfg {
-    static constexpr int D = 128, NW = 8, NT = 64 * NW, BK = 32 * NW, BQ = BQ_;
-    static constexpr int NR = WHICH == 0 ? 1 : 2;        // row tiles: Q (and dO)
-    static constexpr int NV = WHICH == 0 ? 1 : 2;        // row vectors: lse2 (and D), one 1 KiB block each
+struct KvfCfg {
+    static constexpr int D = 128, NW = 8, NT = 64 * NW, BK = 32 * NW / 2, BQ = 64, QB = BQ / 32;
     static constexpr int RROW = 2 * D + 16;
-    static constexpr int RREG = dma_region_bytes(BQ * RROW);
-    static constexpr int R_BLOCKS = (NR * RREG / 1024 + 3) / 4 * 4;
-    static constexpr int T_BLOCKS = BQ * 256 / 1024;    // natural, swizzled rows
-    static constexpr int RSTAGE = R_BLOCKS * 1024, TSTAGE = T_BLOCKS * 1024, LSTAGE = NV * 1024;
-    static constexpr int SMEM = 2 * RSTAGE + 2 * TSTAGE + 3 * LSTAGE;
+    static constexpr int RREG = dma_region_bytes(BQ * RROW);          // 17 KiB: Q rows, then dO rows
+    static constexpr int R_BLOCKS = (2 * RREG / 1024 + 3) / 4 * 4;
+    static constexpr int TREG = BQ * 256;                             // 16 KiB: dO rows, then Q rows
+    static constexpr int T_BLOCKS = 2 * TREG / 1024;
+    static constexpr int RSTAGE = R_BLOCKS * 1024, TSTAGE = T_BLOCKS * 1024, LSTAGE = 2 * 1024;
+    static constexpr int PPAIR = 64 * 16 * 2 * QB;                    // bf16 P of one pair: 64 B a lane
+    static constexpr int SMEM = 2 * RSTAGE + 2 * TSTAGE + 3 * LSTAGE + 4 * PPAIR;
     static constexpr int QREGS = D / 16;
-    static constexpr int QB = BQ / 32;                   // 32-query blocks per tile
     static constexpr int AHEAD = 6;
 };
 
-template <bool CAUSAL, int WHICH, int BQ_>
+template <bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-void bwd_kv_pp_kernel(BParams p) {
-    using C = KvPPCfg<WHICH, BQ_>;
-    constexpr int D = C::D, BK = C::BK, BQ = C::BQ, QB = C::QB, NR = C::NR;
-    static_assert(C::T_BLOCKS % 4 == 0, "LDS-DMA layout");
+void bwd_kvf_kernel(BParams p) {
+    using C = KvfCfg;
+    constexpr int D = C::D, BK = C::BK, BQ = C::BQ, QB = C::QB;
+    static_assert(C::T_BLOCKS % 8 == 0 && C::SMEM <= 160 * 1024, "LDS layout");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
 
     const int tid = threadIdx.x;
@@ -825,34 +824,30 @@ void bwd_kv_pp_kernel(BParams p) {
     const int N = p.N;
     const int kt = blockIdx.x / p.BH;                    // causal: low key tiles see the most queries
     const int bh = blockIdx.x - kt * p.BH;
-    const int k0 = kt * BK, kw0 = k0 + 32 * w, my_k = kw0 + l32;
+    const int k0 = kt * BK, kw0 = k0 + 32 * (w & 3), my_k = kw0 + l32;
 
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* qg = p.q + slice * 2;
     const uint8_t* gg = p.dout + slice * 2;
-    const uint8_t* tg = WHICH == 0 ? gg : qg;            // rows of the transposed operand
     const float* l2g = p.lse2 + static_cast<size_t>(bh) * N;
     const float* dsg = p.dsum + static_cast<size_t>(bh) * N;
 
-    // K (and V) rows of this lane's key: B operands of S = Q K^T (and dP = dO V^T)
-    u32x4 kf[C::QREGS], vf[WHICH == 1 ? C::QREGS : 1];
+    // A: K rows of this lane's key (B operand of S = Q K^T); B: V rows (of dP = dO V^T)
+    u32x4 bf[C::QREGS];
     {
         const bool ok = my_k < N;
-        const size_t off = (slice + static_cast<size_t>(my_k) * D) * 2;
+        const uint8_t* src = (grp == 0 ? p.k : p.v) + (slice + static_cast<size_t>(my_k) * D) * 2;
 #pragma unroll
-        for (int i = 0; i < C::QREGS; ++i) {
-            kf[i] = ok ? ld16(p.k + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
-            if constexpr (WHICH == 1) vf[i] = ok ? ld16(p.v + off + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
-        }
+        for (int i = 0; i < C::QREGS; ++i) bf[i] = ok ? ld16(src + 2 * (16 * i + 8 * h)) : u32x4{0, 0, 0, 0};
     }
 
-    // query tiles [t0, t0 + n_t) of the workgroup; this wave's work starts at local tile j_first
+    // query tiles [t0, t0 + n_t) of the workgroup; this pair's work starts at local tile j_first
     const int n_qt = (N + BQ - 1) / BQ;
     const int t0 = CAUSAL ? min(k0 / BQ, n_qt) : 0;
     const int n_t = n_qt - t0;
     const int j_first = CAUSAL ? min(n_t, kw0 / BQ - t0) : 0;
 
-    // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i)
+    // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i of a stage)
     const uint32_t smem_lds = lds_address(smem);
     const uint32_t rbase = smem_lds, tbase = smem_lds + 2 * C::RSTAGE, lbase = tbase + 2 * C::TSTAGE;
     constexpr int R_PER_W = C::R_BLOCKS / 4, T_PER_W = C::T_BLOCKS / 4, RREG_BLOCKS = C::RREG / 1024;
@@ -861,87 +856,79 @@ void bwd_kv_pp_kernel(BParams p) {
 #pragma unroll
         for (int i = 0; i < R_PER_W; ++i) {
             const int b = (w & 3) + 4 * i;            // Q rows, then dO rows
-            r_off[i] = dma_lane_offset(b % RREG_BLOCKS, lane, D / 8, D * 2, b < NR * RREG_BLOCKS ? BQ : 0);
+            r_off[i] = dma_lane_offset(b % RREG_BLOCKS, lane, D / 8, D * 2, b < 2 * RREG_BLOCKS ? BQ : 0);
         }
         t_off = tr_copy_offset(w, lane);
     }
-    auto copy_r = [&](int j) {                      // rows of tile t0 + j into R stage j % 2, its
-        const int m0 = (t0 + j) * BQ;                // lse2 (and D) into L stage j % 3
+    auto copy_r = [&](int t) {                      // Q, dO rows of local tile t into R stage t % 2,
+        const int m0 = (t0 + t) * BQ;                // its lse2 and D into L stage t % 3
         const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ));
         const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
         const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
-        const uint32_t st = rbase + (j & 1) * C::RSTAGE + 1024 * (w & 3);
+        const uint32_t st = rbase + (t & 1) * C::RSTAGE + 1024 * (w & 3);
 #pragma unroll
         for (int i = 0; i < R_PER_W; ++i) {
             const int b = (w & 3) + 4 * i;
             poison_block(st + 4096 * i);
             lds_dma16(st + 4096 * i, b < RREG_BLOCKS ? rq : rg, r_off[i]);
         }
-        if ((w & 3) < C::NV) {                       // one block per vector, by the first NV copying waves
+        if ((w & 3) < 2) {
             const u32x4 rv = buffer_words((w & 3) == 0 ? l2g + m0 : dsg + m0, valid * 4);
-            const uint32_t lb = lbase + (j % 3) * C::LSTAGE + 1024 * (w & 3);
+            const uint32_t lb = lbase + (t % 3) * C::LSTAGE + 1024 * (w & 3);
             poison_block(lb);
             lds_dma16(lb, rv, lane < BQ / 4 ? 16u * lane : 0x40000000u);
         }
     };
-    auto copy_t = [&](int j) {                      // rows of tile t0 + j, swizzled, into T stage j % 2
-        const int m0 = (t0 + j) * BQ;
-        const u32x4 r = buffer_words(tg + static_cast<size_t>(m0) * D * 2, static_cast<uint32_t>(min(N - m0, BQ)) * D * 2);
-        const uint32_t st = tbase + (j & 1) * C::TSTAGE + 1024 * (w & 3);
+    auto copy_t = [&](int t) {                      // dO, Q rows of local tile t, swizzled, into T stage t % 2
+        const int m0 = (t0 + t) * BQ;
+        const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ)) * D * 2;
+        const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid);
+        const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid);
+        const uint32_t st = tbase + (t & 1) * C::TSTAGE + 1024 * (w & 3);
 #pragma unroll
         for (int i = 0; i < T_PER_W; ++i) {
             poison_block(st + 4096 * i);
-            lds_dma16(st + 4096 * i, r, t_off + 4096 * i);
+            lds_dma16(st + 4096 * i, i < T_PER_W / 2 ? rg : rq, t_off + 4096 * (i % (T_PER_W / 2)));
         }
+    };
+    auto copies = [&](int j) {
+        if (j + 2 < n_t) copy_r(j + 2);
+        if (j + 1 < n_t) copy_t(j + 1);
     };
 
     f32x16 acc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
-    f32x16 s[QB], dp[WHICH == 1 ? QB : 1];
-    uint32_t lane_to[D / 32];                       // transposing reads of the X^T operand
+    f32x16 s[QB];                                    // A: S; B: dP
+    bf16x8 xf[2 * QB];                               // A: P; B: dS
+    uint32_t lane_to[D / 32];                        // transposing reads of the X^T operand
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) lane_to[db] = tr_read_offset(lane, db);
-    bf16x8 xf[2 * QB];
+    uint8_t* pex = smem + 2 * C::RSTAGE + 2 * C::TSTAGE + 3 * C::LSTAGE + (w & 3) * C::PPAIR + 16 * lane;
 
-    // S (and dP) of local tile j, 32-query blocks qb
+    // A: S = Q_t K^T; B: dP = dO_t V^T (local tile j, 32-query blocks qb)
     auto op_s = [&](int j) {
-        const uint8_t* qr = smem + (j & 1) * C::RSTAGE + l32 * C::RROW + 16 * h;
-        constexpr int PER_I = NR * QB;
-        bf16x8 a[PER_I * C::QREGS];
+        const uint8_t* rr = smem + (j & 1) * C::RSTAGE + grp * C::RREG + l32 * C::RROW + 16 * h;
+        bf16x8 a[QB * C::QREGS];
 #pragma unroll
         for (int i = 0; i < C::QREGS; ++i)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                a[PER_I * i + NR * qb] = __builtin_bit_cast(bf16x8, ld16(qr + 32 * qb * C::RROW + 32 * i));
-                if constexpr (WHICH == 1)
-                    a[PER_I * i + NR * qb + 1] = __builtin_bit_cast(bf16x8, ld16(qr + C::RREG + 32 * qb * C::RROW + 32 * i));
-            }
+            for (int qb = 0; qb < QB; ++qb)
+                a[QB * i + qb] = __builtin_bit_cast(bf16x8, ld16(rr + 32 * qb * C::RROW + 32 * i));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            s[qb] = f32x16{};
-            if constexpr (WHICH == 1) dp[qb] = f32x16{};
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
         for (int i = 0; i < C::QREGS; ++i)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PER_I * i + NR * qb], __builtin_bit_cast(bf16x8, kf[i]),
-                                                               s[qb], 0, 0, 0);
-                if constexpr (WHICH == 1)
-                    dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PER_I * i + NR * qb + 1],
-                                                                    __builtin_bit_cast(bf16x8, vf[i]), dp[qb], 0, 0, 0);
-            }
-        pipeline_lds_mfma<PER_I * C::QREGS, C::AHEAD>();
+            for (int qb = 0; qb < QB; ++qb)
+                s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[QB * i + qb], __builtin_bit_cast(bf16x8, bf[i]), s[qb],
+                                                               0, 0, 0);
+        pipeline_lds_mfma<QB * C::QREGS, C::AHEAD>();
     };
-    // P (dK: dS) of local tile j; the query of register v of block qb is
-    // (t0 + j) BQ + 32 qb + acc_row(v, h).  masked: causal, queries before the
-    // key get P = 0; ragged: the tile ends past N, whose queries get P = 0 (a
-    // BQ-query tile may end past the K^T / dO^T padding, which is only rounded
-    // up to 64 keys, and read the next row there)
-    auto op_v = [&](int j, bool masked, bool ragged) {
+    // A: P of local tile j (query of register v of block qb: (t0 + j) BQ + 32 qb +
+    // acc_row(v, h)), 0 before the key (causal, masked) or past N (ragged)
+    auto op_v_a = [&](int j, bool masked, bool ragged) {
         const float* l2s = reinterpret_cast<const float*>(smem + 2 * C::RSTAGE + 2 * C::TSTAGE + (j % 3) * C::LSTAGE);
-        const float* dss = l2s + 256;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int rel = my_k - (t0 + j) * BQ - 32 * qb - 4 * h;   // masked when rel > 8*(v/4) + v%4
@@ -950,14 +937,37 @@ void bwd_kv_pp_kernel(BParams p) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2s + 32 * qb + 8 * g + 4 * h);
-                f32x4 d4 = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (WHICH == 1) d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float pr = fast_exp2(fmaf(s[qb][4 * g + e], p.c_log2, -l4[e]));
+                    if ((masked && rel > 8 * g + e) || (ragged && 8 * g + e > lim)) pr = 0.0f;
+                    x[4 * g + e] = pr;
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xf[2 * qb + cc][e] = static_cast<__bf16>(x[8 * cc + e]);
+                *reinterpret_cast<u32x4*>(pex + 1024 * (2 * qb + cc)) = __builtin_bit_cast(u32x4, xf[2 * qb + cc]);
+            }
+        }
+    };
+    // B: dS = P (dP - D) of local tile j, P as A wrote it
+    auto op_v_b = [&](int j) {
+        const float* dss = reinterpret_cast<const float*>(smem + 2 * C::RSTAGE + 2 * C::TSTAGE + (j % 3) * C::LSTAGE + 1024);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            bf16x8 pb[2];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) pb[cc] = __builtin_bit_cast(bf16x8, ld16(pex + 1024 * (2 * qb + cc)));
+            float x[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(dss + 32 * qb + 8 * g + 4 * h);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g + e;
-                    float pr = fast_exp2(fmaf(s[qb][v], p.c_log2, -l4[e]));
-                    if ((masked && rel > 8 * g + e) || (ragged && 8 * g + e > lim)) pr = 0.0f;
-                    x[v] = WHICH == 0 ? pr : pr * (dp[qb][v] - d4[e]);
+                    x[v] = static_cast<float>(pb[v >> 3][v & 7]) * (s[qb][v] - d4[e]);
                 }
             }
 #pragma unroll
@@ -966,9 +976,9 @@ void bwd_kv_pp_kernel(BParams p) {
                 for (int e = 0; e < 8; ++e) xf[2 * qb + cc][e] = static_cast<__bf16>(x[8 * cc + e]);
         }
     };
-    // acc^T += X^T Y for local tile j
+    // A: dV^T += dO^T P; B: dK^T += Q^T dS (local tile j)
     auto op_acc = [&](int j) {
-        const lds_u8* ts = (const lds_u8*)smem + 2 * C::RSTAGE + (j & 1) * C::TSTAGE;
+        const lds_u8* ts = (const lds_u8*)smem + 2 * C::RSTAGE + (j & 1) * C::TSTAGE + grp * C::TREG;
         constexpr int NC = 2 * QB;                      // 16-query chunks of the tile
         bf16x8 a[NC * (D / 32)];
 #pragma unroll
@@ -986,8 +996,6 @@ void bwd_kv_pp_kernel(BParams p) {
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[NC * db + cc], xf[cc], acc[db], 0, 0, 0);
         pipeline_lds_mfma<NC * (D / 32), C::AHEAD, 2>();
     };
-    // the first tile of the wave is the only one with queries before some of its
-    // keys; the last may end past N
     auto masked_tile = [&](int j) { return CAUSAL && (t0 + j) * BQ < kw0 + 31; };
     auto ragged_tile = [&](int j) { return (t0 + j) * BQ + BQ > N; };
     auto slot_end = [&]() {
@@ -996,7 +1004,7 @@ void bwd_kv_pp_kernel(BParams p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- prologue: group B copies R_0 and waits; everyone meets at barrier 0
+    // ---- prologue: group B copies R_0, L_0 and waits; everyone meets at barrier 0
     if (grp == 1 && n_t > 0) {
         copy_r(0);
         wait_lds_dma();
@@ -1006,21 +1014,21 @@ void bwd_kv_pp_kernel(BParams p) {
     if (n_t > 0) {
         if (grp == 0) {
             // A: M_0 | V_0 M_1 | ... | V_{n-1} M_n | idle, from local tile j_first on
-            for (int j = 0; j < j_first; ++j) {       // queries all before this wave's keys: slots only
+            for (int j = 0; j < j_first; ++j) {
                 slot_end();
                 slot_end();
             }
             if (j_first < n_t) {
                 op_s(j_first);
                 slot_end();
-                op_v(j_first, masked_tile(j_first), ragged_tile(j_first));
+                op_v_a(j_first, masked_tile(j_first), ragged_tile(j_first));
                 slot_end();
                 for (int j = j_first; j + 1 < n_t; ++j) {
                     op_acc(j);
                     __builtin_amdgcn_sched_barrier(0);
                     op_s(j + 1);
                     slot_end();
-                    op_v(j + 1, false, ragged_tile(j + 1));
+                    op_v_a(j + 1, false, ragged_tile(j + 1));
                     slot_end();
                 }
                 op_acc(n_t - 1);
@@ -1029,14 +1037,10 @@ void bwd_kv_pp_kernel(BParams p) {
             slot_end();
         } else {
             // B: copies | M_0 | V_0 + copies, M_1 | ... | V_{n-1} + copies, M_n
-            auto copies = [&](int j) {
-                if (j + 2 < n_t) copy_r(j + 2);
-                if (j + 1 < n_t) copy_t(j + 1);
-            };
             if (1 < n_t) copy_r(1);
             copy_t(0);
             slot_end();
-            for (int j = 0; j < j_first; ++j) {       // copies only
+            for (int j = 0; j < j_first; ++j) {
                 wait_lds_dma();
                 slot_end();
                 copies(j);
@@ -1046,7 +1050,7 @@ void bwd_kv_pp_kernel(BParams p) {
                 op_s(j_first);
                 wait_lds_dma();
                 slot_end();
-                op_v(j_first, masked_tile(j_first), ragged_tile(j_first));
+                op_v_b(j_first);
                 copies(j_first);
                 slot_end();
                 for (int j = j_first; j + 1 < n_t; ++j) {
@@ -1055,7 +1059,7 @@ void bwd_kv_pp_kernel(BParams p) {
                     op_s(j + 1);
                     wait_lds_dma();
                     slot_end();
-                    op_v(j + 1, false, ragged_tile(j + 1));
+                    op_v_b(j + 1);
                     copies(j + 1);
                     slot_end();
                 }
@@ -1067,8 +1071,8 @@ void bwd_kv_pp_kernel(BParams p) {
     }
 
     if (my_k < N) {
-        uint8_t* out = (WHICH == 0 ? p.dv : p.dk) + (slice + static_cast<size_t>(my_k) * D) * 2;
-        const float mul = WHICH == 0 ? 1.0f : p.scale;
+        uint8_t* out = (grp == 0 ? p.dv : p.dk) + (slice + static_cast<size_t>(my_k) * D) * 2;
+        const float mul = grp == 0 ? 1.0f : p.scale;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -1099,9 +1103,11 @@ hipError_t launch_bwd_d(BParams bp, const void* o, const float* lse, float* lse2
     const long long g2 = static_cast<long long>(b.n_tiles) * bp.BH;
     if (g1 > 0x7FFFFFFFLL || g2 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     if constexpr (D == 128) {
-        hipLaunchKernelGGL((bwd_kv_pp_kernel<CAUSAL, 0, kDvSlotQueries>), dim3(static_cast<int>(g2)), dim3(512), 0, st, b);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL((bwd_kv_pp_kernel<CAUSAL, 1, kDkSlotQueries>), dim3(static_cast<int>(g2)), dim3(512), 0, st, b);
+        BParams f = bp;
+        f.n_tiles = (bp.N + KvfCfg::BK - 1) / KvfCfg::BK;
+        const long long g3 = static_cast<long long>(f.n_tiles) * bp.BH;
+        if (g3 > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_kvf_kernel<CAUSAL>), dim3(static_cast<int>(g3)), dim3(KvfCfg::NT), 0, st, f);
     } else {
         hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, 0>), dim3(static_cast<int>(g2)), dim3(KvCfg<D, 0>::NT), 0, st, b);
         if ((e = hipGetLastError()) != hipSuccess) return e;
