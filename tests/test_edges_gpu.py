@@ -75,6 +75,23 @@ def test_forced_rescale_d128(gpu_lib, dtype, causal):
     compare(o, lse, o_ref, lse_ref, dtype, f"{dtype} rescale causal={causal}", lse_tol=lse_tol)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_forced_rescale_d32(gpu_lib, causal):
+    """bf16 d = 32 (its own kernel, whose softmax first tries the current reference
+    without the row max): the score jump makes every query that sees the second
+    half take the full step and rescale O."""
+    N, d = 1024, 32
+    q, k, v = _jump_inputs(N, d, 97)
+    scale = 40.0 / 21.3 ** 2                         # the jump is ~40 in natural units, as at d = 128
+    s = scale * np.einsum("bhid,bhjd->bhij", q.astype(np.float64), k.astype(np.float64))
+    first, second = s[..., : N // 2].max(axis=-1), s[..., N // 2:].max(axis=-1)
+    assert np.all((second - first) * math.log2(math.e) > 45.0), "inputs do not force a rescale"
+    assert np.all(second < 60.0)
+    o, lse = gpu_forward(q, k, v, "bf16", causal, scale)
+    o_ref, lse_ref = oracle_forward(q, k, v, "bf16", causal, scale)
+    compare(o, lse, o_ref, lse_ref, "bf16", f"d=32 rescale causal={causal}")
+
+
 def test_long_single_head_forward(gpu_lib):
     """B = H = 1, N = 262144, d = 64, causal: offsets up to 32 MiB inside one slice."""
     w = Workload("long", 1, 1, 262144, 64, "bf16", True, 91)
