@@ -73,6 +73,10 @@ struct KParams {
     const uint8_t* vscale;
 };
 
+// a float in the constant address space: loads through it with a wave-uniform
+// address become scalar loads (the data is written before the kernel starts)
+typedef __attribute__((address_space(4))) const float const_f32;
+
 // kernel variants of fwd_pp_kernel
 enum : int { kModeDense = 0, kModePartial = 1, kModeSparse = 2 };
 
@@ -682,7 +686,9 @@ void fwd_pp_kernel(KParams p) {
                 }
         }
         float c = c_q;
-        if (FP8) c = c_q / p.k_scale[bh * n_scale + tile_of(j)];     // BN = 64: tile j is scale tile j
+        // BN = 64: tile j is scale tile j (a scalar load and a reciprocal, as in the
+        // 128-key kernel)
+        if (FP8) c = c_q * __builtin_amdgcn_rcpf(((const const_f32*)(p.k_scale))[bh * n_scale + tile_of(j)]);
         float alpha;
         if constexpr (PV8) alpha = softmax_step_p8(s, c, m_run, l_run, p_scale);
         else alpha = softmax_step(s, c, m_run, l_run);
@@ -901,7 +907,7 @@ void fwd_b128_kernel(KParams p) {
     const uint32_t kbase = smem_lds, vbase = smem_lds + 2 * C::KSTAGE;
     uint32_t k_off[C::K_PER_W];
     uint32_t v_off0 = 0;
-    if (grp == 1) {
+    {
 #pragma unroll
         for (int i = 0; i < C::K_PER_W; ++i)
             k_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, D * ES / 16, D * ES, BN);   // past row BN: no data
@@ -1044,9 +1050,13 @@ void fwd_b128_kernel(KParams p) {
         if constexpr (FP8) {
             // 64-key halves carry their own K scales (64-row scale tiles); the second
             // half of the last tile may lie past N (then its scale is never used)
+            // (scalar loads: a vector load's wait would also wait for this wave's
+            // tile copies in flight; a reciprocal instead of an IEEE division, within
+            // an ulp or two)
             const int ks = bh * n_scale + 2 * t;
-            c0 = c_q / p.k_scale[ks];
-            c1 = 2 * t + 1 < n_scale ? c_q / p.k_scale[ks + 1] : c0;
+            const const_f32* kscale = (const const_f32*)(p.k_scale);
+            c0 = c_q * __builtin_amdgcn_rcpf(kscale[ks]);
+            c1 = 2 * t + 1 < n_scale ? c_q * __builtin_amdgcn_rcpf(kscale[ks + 1]) : c0;
         }
         // FP8: past the first tile, the probabilities against the current reference
         // first (softmax_at_ref), the full step only where that fails.  (Measured:
@@ -1087,59 +1097,73 @@ void fwd_b128_kernel(KParams p) {
     // query, and only the last tile can hold keys >= N); the masked tile j_last
     // is peeled off the loops so that the masking code stays out of them.
     const bool last_masked = masked_tile(j_last);
+    // Who copies K_{j+2} and V_{j+1} in slot 2j+2.  bf16: group B, after its
+    // softmax.  FP8: group A, after its MFMAs: the e4m3 S leaves the matrix-core
+    // slot ~1 000 cycles short of the vector slot, and the copies, issued in a
+    // burst that queues behind the CU's address unit, would lengthen the vector
+    // slot that bounds the schedule.  The copying group waits for them at the end
+    // of slot 2j+3.
+    constexpr bool A_COPIES = FP8;
+    auto copies = [&](int j) {
+        if (j + 2 < n_kt) copy_k(j + 2);
+        if (j + 1 < n_kt) copy_v(j + 1);
+    };
     if (grp == 0) {
         // A: M_0 | V_0 M_1 | ... | V_{n-1} M_n | idle
         op_s(0);
         slot_end();
         for (int j = 0; j < j_last; ++j) {
             op_softmax(j, false);
+            if (A_COPIES && j > 0) wait_lds_dma();
             slot_end();
             op_pv(j);
             __builtin_amdgcn_sched_barrier(0);
             op_s(j + 1);
+            if (A_COPIES) copies(j);
             slot_end();
         }
         op_softmax(j_last, last_masked);
+        if (A_COPIES) wait_lds_dma();
         slot_end();
         op_pv(j_last);
+        if (A_COPIES) copies(j_last);
         slot_end();
-        for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: slots only
+        for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: slots (and copies) only
+            if (A_COPIES) wait_lds_dma();
             slot_end();
+            if (A_COPIES) copies(j);
             slot_end();
         }
+        if (A_COPIES) wait_lds_dma();
         slot_end();
     } else {
-        // B: copies | M_0 | V_0 + copies, M_1 | ... | V_{n-1} + copies, M_n
+        // B: copies | M_0 | V_0 (+ copies), M_1 | ... | V_{n-1} (+ copies), M_n
         if (1 < n_kt) copy_k(1);
         copy_v(0);
         slot_end();
         op_s(0);
         wait_lds_dma();
         slot_end();
-        auto copies = [&](int j) {
-            if (j + 2 < n_kt) copy_k(j + 2);
-            if (j + 1 < n_kt) copy_v(j + 1);
-        };
         for (int j = 0; j < j_last; ++j) {
             op_softmax(j, false);
-            copies(j);
+            if (!A_COPIES) copies(j);
             slot_end();
             op_pv(j);
             __builtin_amdgcn_sched_barrier(0);
             op_s(j + 1);
-            wait_lds_dma();
+            if (!A_COPIES) wait_lds_dma();
             slot_end();
         }
         op_softmax(j_last, last_masked);
-        copies(j_last);
+        if (!A_COPIES) copies(j_last);
         slot_end();
         op_pv(j_last);
-        wait_lds_dma();
+        if (!A_COPIES) wait_lds_dma();
         slot_end();
         for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: copies for the others
-            copies(j);
+            if (!A_COPIES) copies(j);
             slot_end();
-            wait_lds_dma();
+            if (!A_COPIES) wait_lds_dma();
             slot_end();
         }
     }
@@ -1352,6 +1376,17 @@ void fwd_d32_kernel(KParams p) {
         const lds_u8* vl = lane_v + (st & 1) * C::STAGE;
         if (t0 < t1) op_s(kl);
         for (int t = t0; t < t1; ++t) {
+            // A wave's issue priority falls as it advances through the stage, so the
+            // four waves sharing a SIMD keep pace with one another.  Left to age
+            // order, the oldest run ahead and the rest finish alone at a fraction of
+            // the SIMD's throughput (measured: waves ending 16-28 us into a 31 us
+            // launch; with this, 21-26 us into 30 us).
+            switch (t - t0) {
+                case 0: __builtin_amdgcn_s_setprio(3); break;
+                case 1: __builtin_amdgcn_s_setprio(2); break;
+                case 2: __builtin_amdgcn_s_setprio(1); break;
+                default: __builtin_amdgcn_s_setprio(0); break;
+            }
             read_v(vl + (t - t0) * BN * C::VROW);
             op_softmax(t);
             if (t + 1 < t1) op_s(kl + (t + 1 - t0) * BN * C::KROW);
