@@ -842,6 +842,11 @@ void fwd_pp_kernel(KParams p) {
 // 2j+3, before the barrier after which group A first reads them.  Copies are
 // LDS-DMA blocks of 1 KiB as in the 64-key kernel.
 // ===========================================================================
+// s_waitcnt vmcnt(N): all but this wave's last N vector-memory loads (here
+// LDS-DMA copies, which complete in issue order) have landed
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 template <bool FP8>
 struct B128Cfg {
     static constexpr int D = 128, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 128;
@@ -855,7 +860,9 @@ struct B128Cfg {
     static constexpr int K_PER_W = K_BLOCKS / 4, V_PER_W = V_BLOCKS / 4;
     // Q fragments per lane: 16 dims per bf16 MFMA; e4m3: 64 dims per MFMA, 32 bytes a lane
     static constexpr int QREGS = FP8 ? 2 * (D / 64) : D / 16;
-    static constexpr int SMEM = 2 * KSTAGE + 2 * VSTAGE;
+    // K stages: FP8 keeps three (see the copy schedule in the kernel), bf16 two
+    static constexpr int KST = FP8 ? 3 : 2;
+    static constexpr int SMEM = KST * KSTAGE + 2 * VSTAGE;
     static constexpr int AHEAD = 9;            // LDS operand lookahead, in MFMAs (9 measured 0.7 % faster than 6)
 };
 
@@ -904,7 +911,7 @@ void fwd_b128_kernel(KParams p) {
     // rows: 16 granules + one pad granule) and of its first V block (V blocks
     // of one wave are 16 key rows = 4 KiB of source apart)
     const uint32_t smem_lds = lds_address(smem);
-    const uint32_t kbase = smem_lds, vbase = smem_lds + 2 * C::KSTAGE;
+    const uint32_t kbase = smem_lds, vbase = smem_lds + C::KST * C::KSTAGE;
     uint32_t k_off[C::K_PER_W];
     uint32_t v_off0 = 0;
     {
@@ -918,7 +925,7 @@ void fwd_b128_kernel(KParams p) {
     auto copy_k = [&](int t) {                    // K_t into K stage t % 2
         const int n0 = t * BN;
         const u32x4 r = buffer_words(kg + static_cast<size_t>(n0) * D * ES, static_cast<uint32_t>(min(N - n0, BN) * D * ES));
-        const uint32_t st = kbase + (t & 1) * C::KSTAGE + 1024 * (w & 3);
+        const uint32_t st = kbase + (t % C::KST) * C::KSTAGE + 1024 * (w & 3);
         static_for<0, C::K_PER_W>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             poison_block(st + 4096 * i);
@@ -956,13 +963,13 @@ void fwd_b128_kernel(KParams p) {
 
     // S^T = K_t Q^T over the 128 keys of tile t
     auto op_s = [&](int t) {
-        const uint8_t* kl = lane_k + (t & 1) * C::KSTAGE;
+        const uint8_t* kl = lane_k + (t % C::KST) * C::KSTAGE;
         if constexpr (FP8) {
             // e4m3: one 32x32x64 MFMA per 32 keys and 64 dims; a lane's 32 bytes of a K row
             // (dims 64i + 32h ..) are two 16-byte reads
             constexpr int NI = D / 64, NA = (BN / 32) * NI;
             i32x8 a[NA];
-            const uint8_t* kf = smem + (t & 1) * C::KSTAGE + l32 * C::KROW + 32 * h;
+            const uint8_t* kf = smem + (t % C::KST) * C::KSTAGE + l32 * C::KROW + 32 * h;
 #pragma unroll
             for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -1017,7 +1024,7 @@ void fwd_b128_kernel(KParams p) {
     auto op_pv = [&](int t) {
         constexpr int NA = (D / 32) * (BN / 16);
         bf16x8 a[NA];
-        const lds_u8* vs = (const lds_u8*)smem + 2 * C::KSTAGE + (t & 1) * C::VSTAGE;
+        const lds_u8* vs = (const lds_u8*)smem + C::KST * C::KSTAGE + (t & 1) * C::VSTAGE;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const lds_u8* vb = vs + lane_vo[db];
@@ -1097,41 +1104,51 @@ void fwd_b128_kernel(KParams p) {
     // query, and only the last tile can hold keys >= N); the masked tile j_last
     // is peeled off the loops so that the masking code stays out of them.
     const bool last_masked = masked_tile(j_last);
-    // Who copies K_{j+2} and V_{j+1} in slot 2j+2.  bf16: group B, after its
-    // softmax.  FP8: group A, after its MFMAs: the e4m3 S leaves the matrix-core
-    // slot ~1 000 cycles short of the vector slot, and the copies, issued in a
-    // burst that queues behind the CU's address unit, would lengthen the vector
-    // slot that bounds the schedule.  The copying group waits for them at the end
-    // of slot 2j+3.
+    // Who copies.  bf16: group B copies K_{j+2} and V_{j+1} in slot 2j+2, after
+    // its softmax, and waits for them at the end of slot 2j+3.  FP8 (e4m3 S, so
+    // the matrix-core slot is ~1 000 cycles shorter than the vector slot): group A
+    // copies, K_{j+2} at the start of its vector slot 2j+1 (into the third K
+    // stage, which K_{j-1} left in slot 2j-1) and V_{j+1} after its MFMAs in slot
+    // 2j+2; at the end of slot 2j+1 it waits for all but the K copies just issued.
+    // Issued in one burst, the copies queue behind the CU's address unit; this
+    // puts that time where the schedule has slack.
     constexpr bool A_COPIES = FP8;
     auto copies = [&](int j) {
         if (j + 2 < n_kt) copy_k(j + 2);
         if (j + 1 < n_kt) copy_v(j + 1);
+    };
+    // A, end of vector slot 2j+1: K_{j+1} and V_j must have landed, K_{j+2} may not
+    auto wait_a = [&](int j) {
+        if (j + 2 < n_kt) wait_vmcnt<C::K_PER_W>();
+        else wait_lds_dma();
     };
     if (grp == 0) {
         // A: M_0 | V_0 M_1 | ... | V_{n-1} M_n | idle
         op_s(0);
         slot_end();
         for (int j = 0; j < j_last; ++j) {
+            if (A_COPIES && j + 2 < n_kt) copy_k(j + 2);
             op_softmax(j, false);
-            if (A_COPIES && j > 0) wait_lds_dma();
+            if (A_COPIES) wait_a(j);
             slot_end();
             op_pv(j);
             __builtin_amdgcn_sched_barrier(0);
             op_s(j + 1);
-            if (A_COPIES) copies(j);
+            if (A_COPIES && j + 1 < n_kt) copy_v(j + 1);
             slot_end();
         }
+        if (A_COPIES && j_last + 2 < n_kt) copy_k(j_last + 2);
         op_softmax(j_last, last_masked);
-        if (A_COPIES) wait_lds_dma();
+        if (A_COPIES) wait_a(j_last);
         slot_end();
         op_pv(j_last);
-        if (A_COPIES) copies(j_last);
+        if (A_COPIES && j_last + 1 < n_kt) copy_v(j_last + 1);
         slot_end();
         for (int j = j_last + 1; j < n_kt; ++j) {     // past the diagonal: slots (and copies) only
-            if (A_COPIES) wait_lds_dma();
+            if (A_COPIES && j + 2 < n_kt) copy_k(j + 2);
+            if (A_COPIES) wait_a(j);
             slot_end();
-            if (A_COPIES) copies(j);
+            if (A_COPIES && j + 1 < n_kt) copy_v(j + 1);
             slot_end();
         }
         if (A_COPIES) wait_lds_dma();
