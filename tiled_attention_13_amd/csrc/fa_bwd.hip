@@ -95,6 +95,31 @@ __device__ __forceinline__ uint32_t tr_read_offset(int lane, int db) {
     return (4 * (g >> 1) + r) * 256 + 64 * (db ^ r) + 16 * (2 * (g & 1) + (j >> 1)) + 8 * (j & 1);
 }
 
+// Row tiles read both ways (rows of 256 bytes, d = 128): by 16-byte row reads
+// (the A operand of an MFMA over the row dimension: lane l reads row l % 32,
+// granule 2i + l / 32) and by the transposing read above.  Granule g of row r
+// sits at xr_granule(r, g) = g ^ (4 (r & 3) + ((r >> 2) & 3)): four
+// consecutive rows fall on four bank quarters, as the transposing reads need,
+// and eight consecutive rows on eight distinct granules, as the row reads
+// need.  (Measured per CU: 4.4 cycles per 1 KiB row read against 4.1 on
+// padded rows and 14.1 under tr_granule; 3.9 cycles per transposing read, as
+// under tr_granule.)
+__device__ __forceinline__ int xr_granule(int row, int g) { return g ^ (4 * (row & 3) + ((row >> 2) & 3)); }
+__device__ __forceinline__ uint32_t xr_copy_offset(int w, int lane) {
+    const int row = 4 * (w & 3) + (lane >> 4);
+    return static_cast<uint32_t>(row * 256 + 16 * xr_granule(row, lane & 15));
+}
+// The transposing reads of such a tile (tr_read_offset's pattern): the offset of
+// the first read; the second read of a chunk (8 rows further on) is at
+// xr_read_offset + xr_hi_delta, because for these rows xr_granule differs from
+// the first read's by 2 in the granule index.
+__device__ __forceinline__ uint32_t xr_read_offset(int lane, int db) {
+    const int g = lane >> 4, r = (lane >> 2) & 3, j = lane & 3;
+    const int row = 4 * (g >> 1) + r;
+    return row * 256 + 16 * xr_granule(row, 4 * db + 2 * (g & 1) + (j >> 1)) + 8 * (j & 1);
+}
+__device__ __forceinline__ int xr_hi_delta(int lane) { return 8 * 256 + (((lane >> 4) & 1) ? -32 : 32); }
+
 // ===========================================================================
 // Pre-pass: D_i = sum_k dO_ik O_ik and lse_i * log2(e), one row per group of
 // D/8 lanes (16 bytes of O and dO per lane).
@@ -788,24 +813,22 @@ __global__ __launch_bounds__(512) void bwd_kv_kernel(BParams p) {
 //   B: M_t = { dK^T += Q_{t-1}^T dS_{t-1},  dP_t = dO_t V^T }
 //      V_t = { dS_t = P_t (dP - D) from A's bf16 P, to bf16 }
 // A runs op k in slot k, B in slot k+1, so P_t is written in slot 2t+1 and
-// read in slot 2t+2.  Row ring (2 stages): Q and dO rows, read in slots 2t,
-// 2t+1; transposed ring (2 stages): dO and Q rows again, natural and swizzled,
-// read with the transposing LDS read in slots 2t+2, 2t+3; vector ring (3
-// stages): lse2 and D, read in slots 2t+1, 2t+2.  Group B copies R_{j+2},
-// L_{j+2} and T_{j+1} in its vector slot 2j+2 and waits for them at the end of
-// slot 2j+3.  Against the split dV and dK kernels this saves the dV kernel's
-// S; dS is formed from the bf16 P (the value P*V sees) instead of the fp32 one.
+// read in slot 2t+2.  Row ring (3 stages): tile t's dO and Q rows, laid out
+// with xr_granule so that S and dP read them as rows (slots 2t, 2t+1) and dV
+// and dK through the transposing read (slots 2t+2, 2t+3); vector ring (3
+// stages): lse2 and D, read in slots 2t+1, 2t+2.  Group B copies X_{j+2} and
+// L_{j+2} in its vector slot 2j+2, into the stages tile j-1 left in slot 2j+1,
+// and waits for them at the end of slot 2j+3.  Against the split dV and dK
+// kernels this saves the dV kernel's S; dS is formed from the bf16 P (the
+// value P*V sees) instead of the fp32 one.
 // ===========================================================================
 struct KvfCfg {
     static constexpr int D = 128, NW = 8, NT = 64 * NW, BK = 32 * NW / 2, BQ = 64, QB = BQ / 32;
-    static constexpr int RROW = 2 * D + 16;
-    static constexpr int RREG = dma_region_bytes(BQ * RROW);          // 17 KiB: Q rows, then dO rows
-    static constexpr int R_BLOCKS = (2 * RREG / 1024 + 3) / 4 * 4;
-    static constexpr int TREG = BQ * 256;                             // 16 KiB: dO rows, then Q rows
-    static constexpr int T_BLOCKS = 2 * TREG / 1024;
-    static constexpr int RSTAGE = R_BLOCKS * 1024, TSTAGE = T_BLOCKS * 1024, LSTAGE = 2 * 1024;
+    static constexpr int XREG = BQ * 256;                             // 16 KiB: dO rows, then Q rows
+    static constexpr int X_BLOCKS = 2 * XREG / 1024;
+    static constexpr int XSTAGE = X_BLOCKS * 1024, LSTAGE = 2 * 1024;
     static constexpr int PPAIR = 64 * 16 * 2 * QB;                    // bf16 P of one pair: 64 B a lane
-    static constexpr int SMEM = 2 * RSTAGE + 2 * TSTAGE + 3 * LSTAGE + 4 * PPAIR;
+    static constexpr int SMEM = 3 * XSTAGE + 3 * LSTAGE + 4 * PPAIR;
     static constexpr int QREGS = D / 16;
     static constexpr int AHEAD = 6;
 };
@@ -815,7 +838,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_kvf_kernel(BParams p) {
     using C = KvfCfg;
     constexpr int D = C::D, BK = C::BK, BQ = C::BQ, QB = C::QB;
-    static_assert(C::T_BLOCKS % 8 == 0 && C::SMEM <= 160 * 1024, "LDS layout");
+    static_assert(C::X_BLOCKS % 8 == 0 && C::SMEM <= 160 * 1024, "LDS layout");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
 
     const int tid = threadIdx.x;
@@ -849,28 +872,19 @@ void bwd_kvf_kernel(BParams p) {
 
     // ---- tile copies (group B, wave w & 3 copies blocks (w & 3) + 4i of a stage)
     const uint32_t smem_lds = lds_address(smem);
-    const uint32_t rbase = smem_lds, tbase = smem_lds + 2 * C::RSTAGE, lbase = tbase + 2 * C::TSTAGE;
-    constexpr int R_PER_W = C::R_BLOCKS / 4, T_PER_W = C::T_BLOCKS / 4, RREG_BLOCKS = C::RREG / 1024;
-    uint32_t r_off[R_PER_W], t_off = 0;
-    if (grp == 1) {
-#pragma unroll
-        for (int i = 0; i < R_PER_W; ++i) {
-            const int b = (w & 3) + 4 * i;            // Q rows, then dO rows
-            r_off[i] = dma_lane_offset(b % RREG_BLOCKS, lane, D / 8, D * 2, b < 2 * RREG_BLOCKS ? BQ : 0);
-        }
-        t_off = tr_copy_offset(w, lane);
-    }
-    auto copy_r = [&](int t) {                      // Q, dO rows of local tile t into R stage t % 2,
+    const uint32_t xbase = smem_lds, lbase = xbase + 3 * C::XSTAGE;
+    constexpr int X_PER_W = C::X_BLOCKS / 4;
+    const uint32_t x_off = grp == 1 ? xr_copy_offset(w, lane) : 0u;
+    auto copy_x = [&](int t) {                      // dO, Q rows of local tile t into X stage t % 3,
         const int m0 = (t0 + t) * BQ;                // its lse2 and D into L stage t % 3
         const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ));
-        const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
         const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
-        const uint32_t st = rbase + (t & 1) * C::RSTAGE + 1024 * (w & 3);
+        const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid * D * 2);
+        const uint32_t st = xbase + (t % 3) * C::XSTAGE + 1024 * (w & 3);
 #pragma unroll
-        for (int i = 0; i < R_PER_W; ++i) {
-            const int b = (w & 3) + 4 * i;
+        for (int i = 0; i < X_PER_W; ++i) {
             poison_block(st + 4096 * i);
-            lds_dma16(st + 4096 * i, b < RREG_BLOCKS ? rq : rg, r_off[i]);
+            lds_dma16(st + 4096 * i, i < X_PER_W / 2 ? rg : rq, x_off + 4096 * (i % (X_PER_W / 2)));
         }
         if ((w & 3) < 2) {
             const u32x4 rv = buffer_words((w & 3) == 0 ? l2g + m0 : dsg + m0, valid * 4);
@@ -879,21 +893,8 @@ void bwd_kvf_kernel(BParams p) {
             lds_dma16(lb, rv, lane < BQ / 4 ? 16u * lane : 0x40000000u);
         }
     };
-    auto copy_t = [&](int t) {                      // dO, Q rows of local tile t, swizzled, into T stage t % 2
-        const int m0 = (t0 + t) * BQ;
-        const uint32_t valid = static_cast<uint32_t>(min(N - m0, BQ)) * D * 2;
-        const u32x4 rg = buffer_words(gg + static_cast<size_t>(m0) * D * 2, valid);
-        const u32x4 rq = buffer_words(qg + static_cast<size_t>(m0) * D * 2, valid);
-        const uint32_t st = tbase + (t & 1) * C::TSTAGE + 1024 * (w & 3);
-#pragma unroll
-        for (int i = 0; i < T_PER_W; ++i) {
-            poison_block(st + 4096 * i);
-            lds_dma16(st + 4096 * i, i < T_PER_W / 2 ? rg : rq, t_off + 4096 * (i % (T_PER_W / 2)));
-        }
-    };
     auto copies = [&](int j) {
-        if (j + 2 < n_t) copy_r(j + 2);
-        if (j + 1 < n_t) copy_t(j + 1);
+        if (j + 2 < n_t) copy_x(j + 2);
     };
 
     f32x16 acc[D / 32];
@@ -903,18 +904,23 @@ void bwd_kvf_kernel(BParams p) {
     bf16x8 xf[2 * QB];                               // A: P; B: dS
     uint32_t lane_to[D / 32];                        // transposing reads of the X^T operand
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) lane_to[db] = tr_read_offset(lane, db);
-    uint8_t* pex = smem + 2 * C::RSTAGE + 2 * C::TSTAGE + 3 * C::LSTAGE + (w & 3) * C::PPAIR + 16 * lane;
+    for (int db = 0; db < D / 32; ++db) lane_to[db] = xr_read_offset(lane, db);
+    const int hi_delta = xr_hi_delta(lane);
+    // row reads of S / dP's A operand (row l32 + 32 qb, granule 2i + h): xr_granule
+    // depends on the row's low four bits only, so qb adds a constant
+    const int xr_row = l32 * 256, xr_fl = 4 * (l32 & 3) + ((l32 >> 2) & 3);
+    uint8_t* pex = smem + 3 * C::XSTAGE + 3 * C::LSTAGE + (w & 3) * C::PPAIR + 16 * lane;
 
     // A: S = Q_t K^T; B: dP = dO_t V^T (local tile j, 32-query blocks qb)
     auto op_s = [&](int j) {
-        const uint8_t* rr = smem + (j & 1) * C::RSTAGE + grp * C::RREG + l32 * C::RROW + 16 * h;
+        // A: Q rows (second half of the stage); B: dO rows (first half)
+        const uint8_t* rr = smem + (j % 3) * C::XSTAGE + (1 - grp) * C::XREG + xr_row;
         bf16x8 a[QB * C::QREGS];
 #pragma unroll
         for (int i = 0; i < C::QREGS; ++i)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)
-                a[QB * i + qb] = __builtin_bit_cast(bf16x8, ld16(rr + 32 * qb * C::RROW + 32 * i));
+                a[QB * i + qb] = __builtin_bit_cast(bf16x8, ld16(rr + 32 * qb * 256 + 16 * ((2 * i + h) ^ xr_fl)));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
@@ -928,7 +934,7 @@ void bwd_kvf_kernel(BParams p) {
     // A: P of local tile j (query of register v of block qb: (t0 + j) BQ + 32 qb +
     // acc_row(v, h)), 0 before the key (causal, masked) or past N (ragged)
     auto op_v_a = [&](int j, bool masked, bool ragged) {
-        const float* l2s = reinterpret_cast<const float*>(smem + 2 * C::RSTAGE + 2 * C::TSTAGE + (j % 3) * C::LSTAGE);
+        const float* l2s = reinterpret_cast<const float*>(smem + 3 * C::XSTAGE + (j % 3) * C::LSTAGE);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             const int rel = my_k - (t0 + j) * BQ - 32 * qb - 4 * h;   // masked when rel > 8*(v/4) + v%4
@@ -954,7 +960,7 @@ void bwd_kvf_kernel(BParams p) {
     };
     // B: dS = P (dP - D) of local tile j, P as A wrote it
     auto op_v_b = [&](int j) {
-        const float* dss = reinterpret_cast<const float*>(smem + 2 * C::RSTAGE + 2 * C::TSTAGE + (j % 3) * C::LSTAGE + 1024);
+        const float* dss = reinterpret_cast<const float*>(smem + 3 * C::XSTAGE + (j % 3) * C::LSTAGE + 1024);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             bf16x8 pb[2];
@@ -978,7 +984,7 @@ void bwd_kvf_kernel(BParams p) {
     };
     // A: dV^T += dO^T P; B: dK^T += Q^T dS (local tile j)
     auto op_acc = [&](int j) {
-        const lds_u8* ts = (const lds_u8*)smem + 2 * C::RSTAGE + (j & 1) * C::TSTAGE + grp * C::TREG;
+        const lds_u8* ts = (const lds_u8*)smem + (j % 3) * C::XSTAGE + grp * C::XREG;
         constexpr int NC = 2 * QB;                      // 16-query chunks of the tile
         bf16x8 a[NC * (D / 32)];
 #pragma unroll
@@ -986,7 +992,7 @@ void bwd_kvf_kernel(BParams p) {
 #pragma unroll
             for (int cc = 0; cc < NC; ++cc) {
                 const i16x4 lo = ds_read_tr16(ts + lane_to[db] + 16 * cc * 256);
-                const i16x4 hi = ds_read_tr16(ts + lane_to[db] + (16 * cc + 8) * 256);
+                const i16x4 hi = ds_read_tr16(ts + lane_to[db] + hi_delta + 16 * cc * 256);
                 a[NC * db + cc] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
 #pragma unroll
@@ -1004,9 +1010,9 @@ void bwd_kvf_kernel(BParams p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- prologue: group B copies R_0, L_0 and waits; everyone meets at barrier 0
+    // ---- prologue: group B copies X_0, L_0 and waits; everyone meets at barrier 0
     if (grp == 1 && n_t > 0) {
-        copy_r(0);
+        copy_x(0);
         wait_lds_dma();
     }
     lds_barrier();
@@ -1037,8 +1043,7 @@ void bwd_kvf_kernel(BParams p) {
             slot_end();
         } else {
             // B: copies | M_0 | V_0 + copies, M_1 | ... | V_{n-1} + copies, M_n
-            if (1 < n_t) copy_r(1);
-            copy_t(0);
+            if (1 < n_t) copy_x(1);
             slot_end();
             for (int j = 0; j < j_first; ++j) {
                 wait_lds_dma();
