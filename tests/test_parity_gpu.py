@@ -48,6 +48,20 @@ def test_d32_stages_and_chunk_pairs(gpu_lib, causal, N):
     compare(o, lse, o_ref, lse_ref, "bf16", f"d=32 N={N} causal={causal}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [257, 300, 384, 640, 1000])
+def test_d128_ring_wraparound(gpu_lib, dtype, causal, N):
+    """At d = 128 the 128-key kernel's rings hold two (bf16) or three (FP8 K)
+    stages and the FP8 copies run two tiles ahead of their first use: these lengths
+    give 3 to 8 key tiles (every stage reused at least once for N >= 384), several
+    query tiles per head, and ragged last tiles."""
+    q, k, v = _small_inputs(dtype, 1, 2, N, 128, seed=5000 + N)
+    o, lse = gpu_forward(q, k, v, dtype, causal, 1.0 / math.sqrt(128))
+    o_ref, lse_ref = oracle_forward(q, k, v, dtype, causal, 1.0 / math.sqrt(128))
+    compare(o, lse, o_ref, lse_ref, dtype, f"d=128 {dtype} N={N} causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 def test_ragged_long_tail(gpu_lib, dtype):
     q, k, v = _small_inputs(dtype, 1, 2, 1000, 64, seed=77)

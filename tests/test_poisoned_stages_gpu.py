@@ -4,10 +4,13 @@ into it is issued, i.e. just after the barrier that ends the last read of
 the stage's previous tile.  A read that lagged behind that barrier or ran
 ahead of the copy's wait would see NaN; with no such race both builds give the
 same bits.  Covered: the bf16 d=128 forward (128-key slots, separate K and V
-rings), the bf16 d=32 forward (256-key stages, two-stage ring, wrapped twice at
-N = 1037), the 64-key LDS-DMA kernels (bf16 at d = 64, FP8, FP8 P*V, split-KV
-partials) and the backward's dK/dV and dQ rings, at d = 32, 64 and 128 and
-small ragged shapes spanning several tiles."""
+rings), the FP8 d=128 forward (three K stages, copies issued by the
+matrix-core group, K two tiles ahead), the bf16 d=32 forward (256-key stages,
+two-stage ring, wrapped twice at N = 1037), the 64-key LDS-DMA kernels (bf16 at
+d = 64, FP8 at d = 32 and 64, FP8 P*V, split-KV partials) and the backward's
+rings (at d = 128 the dK/dV kernel's three-stage ring of rows read both ways,
+and the dQ kernel's rings), at d = 32, 64 and 128 and small ragged shapes
+spanning several tiles."""
 import os
 
 import pytest
