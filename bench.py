@@ -66,7 +66,9 @@ PEAK_HBM_GBPS = 8000.0
 # the forward kernel's code: the HBM traffic summary is valid while these are unchanged
 KERNEL_SOURCES = [os.path.join(ROOT, "tiled_attention_13_amd", "csrc", f)
                   for f in ("fa_fwd.hip", "fa_device.h", "fa_internal.h")]
-COUNTER_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_bf16_counters.json")
+def counter_file(workload: str) -> str:
+    """The committed counter summary of a workload's attention kernel."""
+    return os.path.join(ROOT, "profiles", f"fa_fwd_{workload}_counters.json")
 # rocprofv3 counter passes (each within one run's hardware limits: at most 8 SQ,
 # 2 GRBM and 4 TCC counters; FETCH_SIZE takes 3 TCC counters, WRITE_SIZE 2)
 COUNTER_PASSES = (
@@ -89,7 +91,7 @@ def kernel_source_hash() -> str:
 def committed_counters(workload: str):
     """The committed counter summary, if it was taken on this kernel source and workload."""
     try:
-        with open(COUNTER_FILE) as f:
+        with open(counter_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -403,6 +405,13 @@ def bench_configs(flush_mib: int = 512):
             r["bound"] = "launch latency"
         else:
             r["bound"] = "mfma"
+        t = committed_counters(name)
+        if t is not None:
+            # the committed counter summary of this kernel source (profiles/fa_fwd_<workload>_counters.json)
+            r["counters"] = {k: t[k] for k in ("mfma_busy", "lds_bank_conflict_share", "hbm_bytes_per_launch",
+                                               "kernel_ms_under_profiler")}
+            r["counters"]["hbm_gbps_under_profiler"] = round(t["hbm_bytes_per_launch"] /
+                                                             t["kernel_ms_under_profiler"] / 1e6, 1)
         out[name] = r
         del q, k, v, o, lse
     del flush_buf
@@ -445,6 +454,10 @@ def bench_fp8(steps: int):
                                  "mixed_ceiling_tflops": round(mixed, 1),
                                  "mixed_ceiling_ms": round(w.flops() / (mixed * 1e9), 4),
                                  "valu_estimate_ms": round(scores * VALU_CYCLES_PER_SCORE / N_SIMD / CLOCK_HZ * 1e3, 4)}
+    t = committed_counters("c5_fp8")
+    if t is not None:
+        res["fp8"]["kernel_only"]["counters"] = {k: t[k] for k in ("mfma_busy", "lds_bank_conflict_share",
+                                                                   "hbm_bytes_per_launch", "kernel_ms_under_profiler")}
     res["note"] = ("fp8: Q.K^T on e4m3, P.V on bf16; fp8pv: both on e4m3; ms_per_call includes the "
                    "quantisation pre-passes, kernel_only is fa_fwd_fp8 on pre-quantised Q/K")
     return res

@@ -24,13 +24,13 @@ def test_committed_counters_are_used_only_for_the_source_they_were_taken_on(tmp_
     summary = {"workload": "c4_bf16", "kernel_source_hash": bench.kernel_source_hash(),
                "hbm_bytes_per_launch": 1.5e9, "mfma_busy": 0.5}
     f.write_text(json.dumps(summary))
-    monkeypatch.setattr(bench, "COUNTER_FILE", str(f))
+    monkeypatch.setattr(bench, "counter_file", lambda w: str(f))
     assert bench.committed_counters("c4_bf16")["hbm_bytes_per_launch"] == 1.5e9
-    assert bench.committed_counters("c3_bf16") is None         # another workload
+    assert bench.committed_counters("c3_bf16") is None         # a summary of another workload
     summary["kernel_source_hash"] = "0" * 16                   # counters taken on other sources
     f.write_text(json.dumps(summary))
     assert bench.committed_counters("c4_bf16") is None
-    monkeypatch.setattr(bench, "COUNTER_FILE", str(tmp_path / "missing.json"))
+    monkeypatch.setattr(bench, "counter_file", lambda w: str(tmp_path / "missing.json"))
     assert bench.committed_counters("c4_bf16") is None
 
 
@@ -60,14 +60,19 @@ def test_counter_figures_from_rocprof_rows():
     assert r["hbm_bytes_per_launch"] == r["hbm_fetch_bytes_per_launch"] + r["hbm_write_bytes_per_launch"]
 
 
-def test_committed_counter_summary_matches_the_current_sources():
+def test_committed_counter_summaries_match_the_current_sources():
+    import glob
     import bench
-    with open(bench.COUNTER_FILE) as fh:
-        t = json.load(fh)
-    assert t["kernel_source_hash"] == bench.kernel_source_hash(), \
-        "profiles/fa_fwd_c4_bf16_counters.json was taken on other kernel sources: re-take it (bench.py --write-profile)"
-    assert t["hbm_bytes_per_launch"] == t["hbm_fetch_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
-    assert 0.0 < t["mfma_busy"] < 1.0 and 0.0 <= t["lds_bank_conflict_share"] < 1.0
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "fa_fwd_*_counters.json")))
+    assert bench.counter_file("c4_bf16") in files               # the headline's is always there
+    for path in files:
+        with open(path) as fh:
+            t = json.load(fh)
+        assert path == bench.counter_file(t["workload"])
+        assert t["kernel_source_hash"] == bench.kernel_source_hash(), \
+            f"{os.path.basename(path)} was taken on other kernel sources: re-take it (bench.py --write-profile)"
+        assert t["hbm_bytes_per_launch"] == t["hbm_fetch_bytes_per_launch"] + t["hbm_write_bytes_per_launch"]
+        assert 0.0 < t["mfma_busy"] < 1.0 and 0.0 <= t["lds_bank_conflict_share"] < 1.0
 
 
 def test_cpu_baseline_reports_the_oracle_on_a_bounded_sample():
