@@ -26,8 +26,11 @@ bytes; the d=32 shapes also carry a VALU estimate, their binding roof.
 It also carries a ``backward`` object: ``fa_bwd`` (dQ, dK, dV for a
 seeded upstream gradient) timed the same way on the same bf16 workload,
 with TFLOP/s by the usual convention (2.5 x the forward FLOPs) and the
-matrix-core FLOPs the kernels actually execute (4 x: the dV, dK and dQ
-kernels each recompute S, and dK and dQ both compute dP).
+matrix-core FLOPs the kernels actually execute (3.5 x at d = 128: the dK/dV
+kernel and the dQ kernel each recompute S, and both compute dP).
+A ``power`` object gives the socket power and graphics clock (amdsmi's GPU
+metrics) while the headline calls run back to back for two more seconds,
+untimed, after the timed region; ``--no-power`` skips it.
 
 Hardware counters: before it touches the GPU, the script runs itself three
 times under ``rocprofv3 --pmc`` (one counter pass each, two timed calls after
@@ -463,6 +466,64 @@ def bench_fp8(steps: int):
     return res
 
 
+def sample_power(call, seconds: float = 2.0, settle_s: float = 0.8):
+    """Socket power and graphics clock while `call` runs back to back (untimed).
+
+    Read from amdsmi's GPU metrics table, which the driver refreshes only every
+    few hundred milliseconds: samples from the first `settle_s` seconds of load
+    are dropped, the rest summarised by their median.  Returns {"error": ...}
+    where the library or the metrics are not available."""
+    import threading
+    import torch
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+    except Exception as e:                                  # noqa: BLE001 - any failure is reported
+        return {"error": f"amdsmi: {e!r}"}
+    try:
+        hs = amdsmi.amdsmi_get_processor_handles()
+        if len(hs) != 1:
+            return {"error": f"{len(hs)} devices: the reading could not be tied to the timed one"}
+        h = hs[0]
+        limit = amdsmi.amdsmi_get_power_info(h).get("power_limit")
+        clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            while not stop.is_set():
+                m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+                samples.append((time.perf_counter(), m.get("current_socket_power"), m.get("current_gfxclk")))
+                time.sleep(0.005)
+
+        th = threading.Thread(target=sampler, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(20):
+                call()
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        keep = [(pw, ck) for t, pw, ck in samples if t - t0 >= settle_s
+                and isinstance(pw, (int, float)) and isinstance(ck, (int, float))]
+        if not keep:
+            return {"error": "no metrics samples after the settling time"}
+        return {"socket_power_w": float(np.median([x[0] for x in keep])),
+                "gfxclk_mhz": float(np.median([x[1] for x in keep])),
+                "power_limit_w": round(limit / 1e6, 1) if isinstance(limit, (int, float)) else None,
+                "max_gfxclk_mhz": clk.get("max_clk"),
+                "samples": len(keep), "seconds_under_load": seconds,
+                "source": "amdsmi_get_gpu_metrics_info (current_socket_power, current_gfxclk), "
+                          "untimed calls after the timed region"}
+    except Exception as e:                                  # noqa: BLE001
+        return {"error": f"amdsmi: {e!r}"}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:                                   # noqa: BLE001
+            pass
+
+
 def bench_backward(w, tq, tk, tv, o, lse, steps: int, warmup: int):
     """Time fa_bwd on the resident forward inputs, output and lse (one call = one step)."""
     import torch
@@ -522,6 +583,7 @@ def main():
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the headline fa_fwd (no split-KV, block-sparse or backward objects)")
     ap.add_argument("--no-counters", action="store_true", help="skip the rocprofv3 counter passes")
+    ap.add_argument("--no-power", action="store_true", help="skip the power and clock reading")
     ap.add_argument("--counter-dir", default=None, help="keep the counter passes' raw output here")
     ap.add_argument("--write-profile", default=None, help="write the counter summary (JSON) to this file")
     ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
@@ -590,6 +652,10 @@ def main():
 
     if args.counter_child:
         return
+    # power and clock under the same calls, after the timed region: the headline
+    # runs at the part's power limit, well below its peak clock
+    power = None if args.no_power else sample_power(
+        lambda: fwd(dq, dk, dv, causal=w.causal, dtype=w.dtype, out=out, lse=lse))
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     kern_ms = float(per_call.mean())
@@ -632,6 +698,7 @@ def main():
                      "kernel_ms": round(kern_ms, 4), "per_launch_flops": flops,
                      "algorithmic_bytes": w.compulsory_bytes()},
         "counters": counters,
+        "power": power,
         "input_sha256": digest(q, k, v)[:16],
         "input_gen_s": round(gen_s, 2),
     }
