@@ -50,6 +50,21 @@ def test_d32_stages_and_chunk_pairs(gpu_lib, causal, N):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(2, 8, 300), (3, 8, 700), (2, 24, 513)])
+def test_d128_xcd_banded_order(gpu_lib, dtype, causal, B, H, N):
+    """When B*H is a multiple of 8 and at least two heads' K and V fit in 8 MiB,
+    the 128-key kernel walks each XCD's heads in bands (here 2, 3 and 6 heads per
+    band, with 2 to 3 query tiles per head and ragged ones): every (head, query
+    tile) must be computed exactly once, so the whole output is compared."""
+    q, k, v = _small_inputs(dtype, B, H, N, 128, seed=7000 + N + H)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = gpu_forward(q, k, v, dtype, causal, scale)
+    o_ref, lse_ref = oracle_forward(q, k, v, dtype, causal, scale)
+    compare(o, lse, o_ref, lse_ref, dtype, f"{dtype} B={B} H={H} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [257, 300, 384, 640, 1000])
 def test_d128_ring_wraparound(gpu_lib, dtype, causal, N):
     """At d = 128 the 128-key kernel's rings hold two (bf16) or three (FP8 K)

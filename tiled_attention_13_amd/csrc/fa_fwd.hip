@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -71,7 +73,13 @@ struct KParams {
     int bs_stride;
     // FP8 P*V: MFMA block-scale bytes (127 - e) of the e4m3 V^T, [BH, n_tiles, D]
     const uint8_t* vscale;
+    // d = 128 kernel: heads per band of the XCD-banded work order (0: query-tile major)
+    int band;
 };
+
+// Number of XCDs: consecutive workgroups of a launch go to the eight XCDs in
+// turn, each with its own L2.
+constexpr int kXcds = 8;
 
 // a float in the constant address space: loads through it with a wave-uniform
 // address become scalar loads (the data is written before the kernel starts)
@@ -878,8 +886,23 @@ void fwd_b128_kernel(KParams p) {
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, grp = w >> 2, h = lane >> 5, l32 = lane & 31;
     const int N = p.N;
-    int qt = blockIdx.x / p.BH;
-    const int bh = blockIdx.x - qt * p.BH;
+    // Work item.  Query-tile major (band = 0): workgroup b takes head b mod BH.
+    // XCD-banded (band > 0, BH a multiple of 8): XCD x = b mod 8 runs heads
+    // x + 8m; its k-th workgroup (k = b / 8) is in band k / (band n_qtiles),
+    // which holds `band` of those heads, walked query tile by query tile
+    // (heaviest first when causal) across the band's heads.  A band's K and V
+    // stay within the XCD's L2 while its query tiles stream them.
+    int qt, bh;
+    if (p.band > 0) {
+        const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+        const int per_band = p.band * p.n_qtiles;
+        const int band = k / per_band, r = k - band * per_band;
+        qt = r / p.band;
+        bh = x + kXcds * (band * p.band + (r - qt * p.band));
+    } else {
+        qt = blockIdx.x / p.BH;
+        bh = blockIdx.x - qt * p.BH;
+    }
     if (CAUSAL) qt = p.n_qtiles - 1 - qt;        // heaviest query tiles first
     const int q0 = qt * BM, qw0 = q0 + 32 * w, my_q = qw0 + l32;
     const size_t slice = static_cast<size_t>(bh) * N * D;
@@ -1773,6 +1796,20 @@ template <bool CAUSAL, bool FP8>
 hipError_t launch_b128(KParams kp, int BH, hipStream_t st) {
     using C = B128Cfg<FP8>;
     kp.n_qtiles = (kp.N + C::BM - 1) / C::BM;
+    // XCD-banded order where every XCD gets the same heads: bands of as many of
+    // an XCD's heads as keep their K and V within 8 MiB (twice one XCD's L2:
+    // the band's query tiles stream them roughly in step), if that is at least
+    // two.  (Measured at 4x32x4096x128 causal, 2 MiB of K and V per head: bands
+    // of 1 / 2 / 4 / 8 heads +2.5 / -1.9 / -3.0 / -2.5 % against query-tile
+    // major; at 1x32x16384x128, 8 MiB per head: bands of 1 +0.9 %.)
+    kp.band = 0;
+    if (BH % kXcds == 0) {
+        const int per_xcd = BH / kXcds;
+        const long long kv = static_cast<long long>(kp.N) * C::D * (C::ES + 2);
+        int band = static_cast<int>(std::min<long long>(per_xcd, (8LL << 20) / kv));
+        while (band > 1 && per_xcd % band != 0) --band;
+        kp.band = band >= 2 ? band : 0;
+    }
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fwd_b128_kernel<CAUSAL, FP8>), dim3(static_cast<int>(grid)), dim3(C::NT), 0, st, kp);
@@ -1914,6 +1951,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
     kp.bs_count = a.bs_count;
     kp.bs_stride = a.bs_stride;
     kp.vscale = a.v_scale;
+    kp.band = 0;
     if (a.kind == Kind::FP8PV && (a.v_scale == nullptr || a.o32 != nullptr || a.bs_list != nullptr))
         return hipErrorInvalidValue;
     if (a.o32 != nullptr && (a.kind != Kind::BF16 || a.n_splits < 1 || a.tps < 1)) return hipErrorInvalidValue;
