@@ -195,7 +195,7 @@ def derive_counters(rows: dict, m: str) -> dict:
         "gui_cycles_per_launch": round(cycles),
         "kernel_ms_under_profiler": round(dur_ns / 1e6, 4),
         "hbm_fetch_bytes_per_launch": round(fetch_b), "hbm_write_bytes_per_launch": round(write_b),
-        "hbm_bytes_per_launch": round(fetch_b + write_b),
+        "hbm_bytes_per_launch": round(fetch_b) + round(write_b),
         "calibration": {"kernel": cf[-1][3], "bytes_read_and_written": calib_bytes,
                         "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4)},
         "definitions": "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE/8); "
