@@ -890,8 +890,9 @@ void fwd_b128_kernel(KParams p) {
     // XCD-banded (band > 0, BH a multiple of 8): XCD x = b mod 8 runs heads
     // x + 8m; its k-th workgroup (k = b / 8) is in band k / (band n_qtiles),
     // which holds `band` of those heads, walked query tile by query tile
-    // (heaviest first when causal) across the band's heads.  A band's K and V
-    // stay within the XCD's L2 while its query tiles stream them.
+    // (heaviest first when causal) across the band's heads.  The query tiles
+    // of a band stream the same few heads' K and V at about the same time, so
+    // the XCD's L2 serves most of their reads.
     int qt, bh;
     if (p.band > 0) {
         const int x = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
@@ -1702,15 +1703,23 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     const size_t base = (static_cast<size_t>(bh) * N + r0) * D;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + base);
 
+    // the whole tile (at most 64 rows x 128 dims: four 16-byte chunks a thread)
+    // is loaded at once and kept in registers for the conversion
+    constexpr int PER_T = 64 * 128 / 8 / 256;
+    u32x4 u[PER_T];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        u[i] = c < n_chunks ? src[c] : u32x4{0u, 0u, 0u, 0u};
+    }
     float amax = 0.0f;
-    for (int c = threadIdx.x; c < n_chunks; c += 256) {
-        const u32x4 u = src[c];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i)
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
-            amax = fmaxf(amax, fabsf(__uint_as_float(u[wd] << 16)));
-            amax = fmaxf(amax, fabsf(__uint_as_float(u[wd] & 0xFFFF0000u)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(u[i][wd] << 16)));
+            amax = fmaxf(amax, fabsf(__uint_as_float(u[i][wd] & 0xFFFF0000u)));
         }
-    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
@@ -1720,12 +1729,14 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const uint16_t* __restri
     if (threadIdx.x == 0) scale[tile] = s;
 
     u32x2* dst = reinterpret_cast<u32x2*>(x8 + base);
-    for (int c = threadIdx.x; c < n_chunks; c += 256) {
-        const u32x4 u = src[c];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c >= n_chunks) break;
         uint32_t packed[2] = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const uint32_t hb = (e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16);
+            const uint32_t hb = (e & 1) ? (u[i][e >> 1] & 0xFFFF0000u) : (u[i][e >> 1] << 16);
             float y = __uint_as_float(hb) * s;
             y = fminf(fmaxf(y, -448.0f), 448.0f);
             packed[e >> 2] |= e4m3_code(y) << (8 * (e & 3));
@@ -2028,6 +2039,7 @@ hipError_t launch_quant_fp8(const void* x_bf16, uint8_t* x8, float* scale, int B
     const int n_tiles = (N + 63) / 64;
     const long long grid = static_cast<long long>(BH) * n_tiles;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+    if (d > 128 || d % 8 != 0) return hipErrorInvalidValue;    // a tile is at most four chunks a thread
     hipLaunchKernelGGL(quant_fp8_kernel, dim3(static_cast<int>(grid)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(x_bf16), x8, scale, N, d, n_tiles);
     return hipGetLastError();
