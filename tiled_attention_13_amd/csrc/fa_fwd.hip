@@ -1757,23 +1757,51 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_v_pow2_kernel(const uint8_t* __restrict__ v, uint8_t* __restrict__ v8,
                                                            uint8_t* __restrict__ vscale, int N, int np, int n_tiles) {
     constexpr int ROW = 2 * D + 16;
+    constexpr int CPR = D / 8;                     // 16-byte chunks per key row
+    constexpr int PER_T = kKeyTile * CPR / 256;    // chunks per thread
+    static_assert(PER_T >= 1 && 256 % CPR == 0, "tile split");
     __shared__ __attribute__((aligned(16))) uint8_t tile[kKeyTile * ROW];
+    __shared__ float wmax[4][D];                   // per-wave column maxima
     __shared__ int sexp[D];
     const int bh = blockIdx.x / n_tiles, t = blockIdx.x - bh * n_tiles;
     const int n0 = kKeyTile * t;
     const uint8_t* src = v + (static_cast<size_t>(bh) * N + n0) * D * 2;
-    for (int c = threadIdx.x; c < kKeyTile * D / 8; c += 256) {
-        const int key = c / (D / 8), col = c - key * (D / 8);
-        const u32x4 x = n0 + key < N ? ld16(src + (key * D + 8 * col) * 2) : u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(tile + key * ROW + 16 * col) = x;
+    // every chunk of the tile is loaded at once; a thread's chunks share one
+    // column group (dims 8 col ..), whose magnitudes it folds into pm as they go
+    // to LDS
+    const int col = static_cast<int>(threadIdx.x) % CPR;
+    u32x4 x[PER_T];
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int key = (static_cast<int>(threadIdx.x) + 256 * i) / CPR;
+        x[i] = n0 + key < N ? ld16(src + (key * D + 8 * col) * 2) : u32x4{0, 0, 0, 0};
+    }
+    float pm[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < PER_T; ++i) {
+        const int key = (static_cast<int>(threadIdx.x) + 256 * i) / CPR;
+        *reinterpret_cast<u32x4*>(tile + key * ROW + 16 * col) = x[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t hb = (e & 1) ? (x[i][e >> 1] & 0xFFFF0000u) : (x[i][e >> 1] << 16);
+            pm[e] = fmaxf(pm[e], fabsf(__uint_as_float(hb)));
+        }
+    }
+    // lanes of a wave with the same column group, then the four waves
+#pragma unroll
+    for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pm[e] = fmaxf(pm[e], __shfl_xor(pm[e], off));
+    if ((threadIdx.x & 63) < CPR) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wmax[threadIdx.x >> 6][8 * col + e] = pm[e];
     }
     __syncthreads();
     auto val = [&](int key, int d) -> float {
         return __uint_as_float(static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(tile + key * ROW + 2 * d)) << 16);
     };
     for (int d = threadIdx.x; d < D; d += 256) {
-        float amax = 0.0f;
-        for (int key = 0; key < kKeyTile; ++key) amax = fmaxf(amax, fabsf(val(key, d)));
+        const float amax = fmaxf(fmaxf(wmax[0][d], wmax[1][d]), fmaxf(wmax[2][d], wmax[3][d]));
         int e = 0;
         if (amax > 0.0f) {
             int x;
