@@ -132,8 +132,9 @@ def kernel_match(w) -> str:
     """Substring of the attention kernel's name in rocprofv3 output for a workload."""
     if w.dtype == "f32":
         return "fwd_f32_kernel"
-    if w.dtype in ("bf16", "fp8") and w.d == 128:
-        return f"fwd_b128_kernel<{'true' if w.causal else 'false'}, {'true' if w.dtype == 'fp8' else 'false'}>"
+    if w.d == 128:
+        tf = lambda b: "true" if b else "false"
+        return f"fwd_b128_kernel<{tf(w.causal)}, {tf(w.dtype != 'bf16')}, {tf(w.dtype == 'fp8pv')}>"
     if w.dtype == "bf16" and w.d == 32:
         return f"fwd_d32_kernel<{'true' if w.causal else 'false'}"
     return f"fwd_pp_kernel<{w.d}, {'true' if w.causal else 'false'}, {'true' if w.dtype != 'bf16' else 'false'}, 0"
@@ -461,6 +462,10 @@ def bench_fp8(steps: int):
     if t is not None:
         res["fp8"]["kernel_only"]["counters"] = {k: t[k] for k in ("mfma_busy", "lds_bank_conflict_share",
                                                                    "hbm_bytes_per_launch", "kernel_ms_under_profiler")}
+    t = committed_counters("c5_fp8pv")
+    if t is not None:
+        res["fp8pv"]["counters"] = {k: t[k] for k in ("mfma_busy", "lds_bank_conflict_share",
+                                                      "hbm_bytes_per_launch", "kernel_ms_under_profiler")}
     res["note"] = ("fp8: Q.K^T on e4m3, P.V on bf16; fp8pv: both on e4m3; ms_per_call includes the "
                    "quantisation pre-passes, kernel_only is fa_fwd_fp8 on pre-quantised Q/K")
     return res

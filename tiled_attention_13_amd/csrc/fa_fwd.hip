@@ -223,6 +223,44 @@ __device__ __forceinline__ float softmax_step_p8(float (&s)[NS], float c, float&
     return alpha;
 }
 
+// The same for a 128-key tile as two 64-key halves, each a scale tile of its
+// own (the first NS/2 scores scaled into base-2 units by c0, the rest by c1):
+// one reference for the tile, one 2^f per half, scale_b[h] = 127 - f of half h.
+template <int NS>
+__device__ __forceinline__ float softmax_step_p8x2(float (&s)[NS], float c0, float c1, float& m, float& l,
+                                                   int (&scale_b)[2]) {
+    float ma = kNegInf, mb = kNegInf;
+#pragma unroll
+    for (int i = 0; i < NS / 2; ++i) ma = fmaxf(ma, s[i]);
+#pragma unroll
+    for (int i = NS / 2; i < NS; ++i) mb = fmaxf(mb, s[i]);
+    const float ha = max_halves(ma) * c0, hb = max_halves(mb) * c1;
+    const float mx2 = fmaxf(ha, hb);
+    float alpha = 1.0f;
+    if (mx2 > m + kRescaleSlack) {
+        alpha = fast_exp2(m - mx2);
+        m = mx2;
+    }
+    const float m_use = (m == kNegInf) ? 0.0f : m;
+    l *= alpha;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const float fl = floorf(8.807354922f - ((hf ? hb : ha) - m_use));
+        const int f = fl > 126.0f ? 126 : (fl < -126.0f ? -126 : static_cast<int>(fl));   // -inf half: 126
+        const float shift = static_cast<float>(f) - m_use, c = hf ? c1 : c0;
+        float rs = 0.0f;
+#pragma unroll
+        for (int i = hf * NS / 2; i < (hf + 1) * NS / 2; ++i) {
+            const float pr = fast_exp2(fmaf(s[i], c, shift));
+            s[i] = pr;
+            rs += pr;
+        }
+        l = fmaf(rs, __int_as_float((127 - f) << 23), l);      // rs * 2^-f
+        scale_b[hf] = 127 - f;
+    }
+    return alpha;
+}
+
 // 16-byte granule of a bf16 V key row in LDS: data granule g of key row `row`
 // sits at granule v_granule<D>(row, g), an XOR and so its own inverse.  The
 // transposing reads of the P*V operand take, per 32 lanes, four consecutive
@@ -859,15 +897,21 @@ void fwd_pp_kernel(KParams p) {
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-template <bool FP8>
+template <bool FP8, bool PV8 = false>
 struct B128Cfg {
     static constexpr int D = 128, NW = 8, NT = 64 * NW, BM = 32 * NW, BN = 128;
     static constexpr int ES = FP8 ? 1 : 2;     // bytes per Q/K element (e4m3 or bf16)
-    static constexpr int KROW = D * ES + 16, VROW = D * 2;
+    // V: BN natural bf16 key rows; e4m3 P*V: D rows of V^T, BN keys plus one pad granule
+    static constexpr int KROW = D * ES + 16, VROW = PV8 ? BN + 16 : D * 2;
     // a K stage holds BN padded rows (34 KiB, e4m3 18 KiB); it is rounded up to
     // whole groups of four blocks so that each of the four copying waves issues
-    // the same number (the last blocks carry no data)
-    static constexpr int K_BLOCKS = (BN * KROW + 4095) / 4096 * 4, V_BLOCKS = BN * VROW / 1024;
+    // the same number (the last blocks carry no data).  An e4m3 V^T stage is
+    // 18 KiB of rows, then one block whose first 2 x D bytes are the block
+    // exponents of the tile's two 64-key halves, rounded up the same way.
+    static constexpr int K_BLOCKS = (BN * KROW + 4095) / 4096 * 4;
+    static constexpr int V_DATA = (PV8 ? D : BN) * VROW / 1024;
+    static constexpr int V_BLOCKS = PV8 ? (V_DATA + 1 + 3) / 4 * 4 : V_DATA;
+    static constexpr int VSCALE = V_DATA * 1024;    // e4m3 P*V: byte offset of the exponents in a V stage
     static constexpr int KSTAGE = K_BLOCKS * 1024, VSTAGE = V_BLOCKS * 1024;
     static constexpr int K_PER_W = K_BLOCKS / 4, V_PER_W = V_BLOCKS / 4;
     // Q fragments per lane: 16 dims per bf16 MFMA; e4m3: 64 dims per MFMA, 32 bytes a lane
@@ -878,12 +922,13 @@ struct B128Cfg {
     static constexpr int AHEAD = 9;            // LDS operand lookahead, in MFMAs (9 measured 0.7 % faster than 6)
 };
 
-template <bool CAUSAL, bool FP8>
+template <bool CAUSAL, bool FP8, bool PV8 = false>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void fwd_b128_kernel(KParams p) {
-    using C = B128Cfg<FP8>;
+    using C = B128Cfg<FP8, PV8>;
     constexpr int D = C::D, BM = C::BM, BN = C::BN, ES = C::ES;
     static_assert(C::KSTAGE % 1024 == 0 && C::VSTAGE % 4096 == 0, "LDS-DMA layout");
+    static_assert(!PV8 || (FP8 && C::D * C::VROW == C::V_DATA * 1024), "e4m3 P*V: e4m3 S, whole V^T blocks");
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
 
     const int tid = threadIdx.x;
@@ -913,7 +958,8 @@ void fwd_b128_kernel(KParams p) {
     const size_t slice = static_cast<size_t>(bh) * N * D;
     const uint8_t* qg = p.q + slice * ES;
     const uint8_t* kg = p.k + slice * ES;
-    const uint8_t* vg = p.v + slice * 2;
+    // V rows of this (b, h), or (e4m3 P*V) its e4m3 V^T: D rows of np keys
+    const uint8_t* vg = PV8 ? p.vt + static_cast<size_t>(bh) * D * p.np : p.v + slice * 2;
 
     // Q fragments (B operand): bf16 dims 16i + 8h .. +7; e4m3 dims 64(i/2) + 32h + 16(i%2) .. +15
     u32x4 qf[C::QREGS];
@@ -942,12 +988,23 @@ void fwd_b128_kernel(KParams p) {
     const uint32_t kbase = smem_lds, vbase = smem_lds + C::KST * C::KSTAGE;
     uint32_t k_off[C::K_PER_W];
     uint32_t v_off0 = 0;
+    // e4m3 V^T: per-lane offsets of this wave's V blocks (rows of np keys: D rows of
+    // 8 granules + one pad granule, then the exponent block: 16 lanes of 16 bytes)
+    uint32_t v_off8[PV8 ? C::V_PER_W : 1];
     {
 #pragma unroll
         for (int i = 0; i < C::K_PER_W; ++i)
             k_off[i] = dma_lane_offset((w & 3) + 4 * i, lane, D * ES / 16, D * ES, BN);   // past row BN: no data
         const int row = 4 * (w & 3) + (lane >> 4);
         v_off0 = row * (D * 2) + 16 * v_granule<D>(row, lane & 15);
+        if constexpr (PV8) {
+#pragma unroll
+            for (int i = 0; i < C::V_PER_W; ++i) {
+                const int b = (w & 3) + 4 * i, g = 64 * b + lane, vr = g / (BN / 16 + 1), col = g - (BN / 16 + 1) * vr;
+                v_off8[i] = b < C::V_DATA ? (col < BN / 16 ? static_cast<uint32_t>(vr) * p.np + 16 * col : 0x40000000u)
+                                          : (b == C::V_DATA && lane < 2 * D / 16 ? 16u * lane : 0x40000000u);
+            }
+        }
     }
     // block (w & 3) + 4i of a stage: LDS byte 1024 (w & 3) + 4096 i of it
     auto copy_k = [&](int t) {                    // K_t into K stage t % 2
@@ -962,8 +1019,29 @@ void fwd_b128_kernel(KParams p) {
     };
     auto copy_v = [&](int t) {                    // V_t into V stage t % 2; its rows 16 i further on
         const int n0 = t * BN;
-        const u32x4 r = buffer_words(vg + static_cast<size_t>(n0) * D * 2, static_cast<uint32_t>(min(N - n0, BN) * D * 2));
         const uint32_t st = vbase + (t & 1) * C::VSTAGE + 1024 * (w & 3);
+        if constexpr (PV8) {
+            // e4m3 V^T columns n0 .. n0 + BN (past np: zero or the next row's codes,
+            // met by P = 0) and the exponents of 64-key tiles 2t, 2t + 1 (past the
+            // last: 0, a finite 2^-127)
+            const int n64 = (N + 63) / 64;
+            const u32x4 r = buffer_words(vg + n0, static_cast<uint32_t>(D) * p.np - n0);
+            const u32x4 rs = buffer_words(p.vscale + (static_cast<size_t>(bh) * n64 + 2 * t) * D,
+                                          static_cast<uint32_t>(min(2, n64 - 2 * t) * D));
+            // blocks of the last round: data for waves with (w & 3) + 4 i < V_DATA, the
+            // exponents for the next one, nothing (offset past every range) after it
+            static_assert(C::V_DATA >= 4 * (C::V_PER_W - 1) && C::V_DATA < 4 * C::V_PER_W, "one mixed round");
+            const bool last_data = (w & 3) < C::V_DATA - 4 * (C::V_PER_W - 1);
+            const u32x4 rl = {last_data ? r[0] : rs[0], last_data ? r[1] : rs[1], last_data ? r[2] : rs[2],
+                              last_data ? r[3] : rs[3]};
+            static_for<0, C::V_PER_W>([&](auto ic) {
+                constexpr int i = decltype(ic)::value;
+                poison_block(st + 4096 * i);
+                lds_dma16_at<4096 * i, 0>(st, i + 1 < C::V_PER_W ? r : rl, v_off8[i]);
+            });
+            return;
+        }
+        const u32x4 r = buffer_words(vg + static_cast<size_t>(n0) * D * 2, static_cast<uint32_t>(min(N - n0, BN) * D * 2));
         static_for<0, C::V_PER_W>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
             poison_block(st + 4096 * i);
@@ -979,6 +1057,8 @@ void fwd_b128_kernel(KParams p) {
     float m_run = kNegInf, l_run = 0.0f;
     float s[BN / 2];
     bf16x8 pf[BN / 16];
+    uint32_t pf8[2][8];                           // e4m3 P*V: P^T of each 64-key half, e4m3 codes
+    int p_scale[2] = {127, 127};                  // and their block exponents (127 - f)
 
     const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
     uint32_t lane_vo[D / 32];
@@ -1050,6 +1130,29 @@ void fwd_b128_kernel(KParams p) {
     };
     // O^T += V_t^T P_t^T
     auto op_pv = [&](int t) {
+        if constexpr (PV8) {
+            // one 32x32x64 e4m3 MFMA per 64-key half and 32 rows of d; A = 32 bytes of a
+            // V^T row (keys 32h .. of the half, in the P operand's key order), both
+            // operands scaled by their block exponents
+            const uint8_t* vl = smem + C::KST * C::KSTAGE + (t & 1) * C::VSTAGE;
+            const uint8_t* sc = vl + C::VSCALE;
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const i32x8 b = {(int)pf8[hf][0], (int)pf8[hf][1], (int)pf8[hf][2], (int)pf8[hf][3],
+                                 (int)pf8[hf][4], (int)pf8[hf][5], (int)pf8[hf][6], (int)pf8[hf][7]};
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const uint8_t* ap = vl + (32 * db + l32) * C::VROW + 64 * hf + 32 * h;
+                    const u32x4 a0 = ld16(ap), a1 = ld16(ap + 16);
+                    const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                                     (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+                    const int sa = sc[D * hf + 32 * db + l32];
+                    o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, o[db], 0, 0, 0, sa, 0, p_scale[hf]);
+                }
+            }
+            pipeline_lds_mfma<2 * (D / 32), 3, 3>();    // two operand reads and the exponent byte per MFMA
+            return;
+        }
         constexpr int NA = (D / 32) * (BN / 16);
         bf16x8 a[NA];
         const lds_u8* vs = (const lds_u8*)smem + C::KST * C::KSTAGE + (t & 1) * C::VSTAGE;
@@ -1092,6 +1195,27 @@ void fwd_b128_kernel(KParams p) {
             const const_f32* kscale = (const const_f32*)(p.k_scale);
             c0 = c_q * __builtin_amdgcn_rcpf(kscale[ks]);
             c1 = 2 * t + 1 < n_scale ? c_q * __builtin_amdgcn_rcpf(kscale[ks + 1]) : c0;
+        }
+        if constexpr (PV8) {
+            // the scale of each half's probabilities needs that half's max: always the full step
+            const float alpha = softmax_step_p8x2(s, c0, c1, m_run, l_run, p_scale);
+            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+            }
+            // byte 4 wd + k of half hf's B operand is s[32 hf + 4 wd + k] (register order =
+            // the key order of the e4m3 V^T rows)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int wd = 0; wd < 8; ++wd) {
+                    int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[32 * hf + 4 * wd], s[32 * hf + 4 * wd + 1], 0, false);
+                    x = __builtin_amdgcn_cvt_pk_fp8_f32(s[32 * hf + 4 * wd + 2], s[32 * hf + 4 * wd + 3], x, true);
+                    pf8[hf][wd] = static_cast<uint32_t>(x);
+                }
+            return;
         }
         // FP8: past the first tile, the probabilities against the current reference
         // first (softmax_at_ref), the full step only where that fails.  (Measured:
@@ -1835,9 +1959,9 @@ __global__ __launch_bounds__(256) void quant_v_pow2_kernel(const uint8_t* __rest
 }
 
 
-template <bool CAUSAL, bool FP8>
+template <bool CAUSAL, bool FP8, bool PV8 = false>
 hipError_t launch_b128(KParams kp, int BH, hipStream_t st) {
-    using C = B128Cfg<FP8>;
+    using C = B128Cfg<FP8, PV8>;
     kp.n_qtiles = (kp.N + C::BM - 1) / C::BM;
     // XCD-banded order where every XCD gets the same heads: bands of as many of
     // an XCD's heads as keep their K and V within 8 MiB (twice one XCD's L2:
@@ -1848,14 +1972,14 @@ hipError_t launch_b128(KParams kp, int BH, hipStream_t st) {
     kp.band = 0;
     if (BH % kXcds == 0) {
         const int per_xcd = BH / kXcds;
-        const long long kv = static_cast<long long>(kp.N) * C::D * (C::ES + 2);
+        const long long kv = static_cast<long long>(kp.N) * C::D * (C::ES + (PV8 ? 1 : 2));
         int band = static_cast<int>(std::min<long long>(per_xcd, (8LL << 20) / kv));
         while (band > 1 && per_xcd % band != 0) --band;
         kp.band = band >= 2 ? band : 0;
     }
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
     if (grid > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_b128_kernel<CAUSAL, FP8>), dim3(static_cast<int>(grid)), dim3(C::NT), 0, st, kp);
+    hipLaunchKernelGGL((fwd_b128_kernel<CAUSAL, FP8, PV8>), dim3(static_cast<int>(grid)), dim3(C::NT), 0, st, kp);
     return hipGetLastError();
 }
 
@@ -1887,6 +2011,7 @@ hipError_t launch_bf(KParams kp, int BH, hipStream_t st) {
 }
 template <int D, bool CAUSAL>
 hipError_t launch_fp8pv(KParams kp, int BH, hipStream_t st) {
+    if constexpr (D == 128) return launch_b128<CAUSAL, true, true>(kp, BH, st);
     using C = PPCfg<D, CAUSAL, true, true>;
     kp.n_qtiles = (kp.N + C::BM - 1) / C::BM;
     const long long grid = static_cast<long long>(kp.n_qtiles) * BH;
