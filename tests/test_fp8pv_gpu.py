@@ -72,6 +72,32 @@ def test_small_shapes(gpu_lib, d, causal, N):
     _check(o, lse, o_ref, lse_ref, a, f"fp8pv d={d} causal={causal} N={N}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(2, 8, 300), (3, 8, 700), (2, 24, 513)])
+def test_d128_xcd_banded_order(gpu_lib, causal, B, H, N):
+    """B*H a multiple of 8 with short heads: the 128-key kernel walks each XCD's
+    heads in bands of 2, 3 and 6, with ragged query tiles; every (head, query
+    tile) must be computed exactly once, so the whole output is compared."""
+    q, k, v = make_inputs(Workload("band", B, H, N, 128, "bf16", False, 7100 + N + H))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _gpu(q, k, v, causal, scale)
+    o_ref, lse_ref, a = _oracle_fp8pv(q, k, v, causal, scale)
+    _check(o, lse, o_ref, lse_ref, a, f"fp8pv B={B} H={H} N={N} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [130, 257, 384, 640, 1000])
+def test_d128_ring_wraparound(gpu_lib, causal, N):
+    """The 128-key kernel's V ring holds two stages of e4m3 V^T rows plus the
+    exponents of their two 64-key tiles: 2 to 8 key tiles, every stage reused for
+    N >= 384, and last tiles holding one 64-key tile (130, 257) or a ragged one (1000)."""
+    q, k, v = make_inputs(Workload("ring", 1, 2, N, 128, "bf16", False, 7200 + N))
+    scale = 1.0 / math.sqrt(128)
+    o, lse = _gpu(q, k, v, causal, scale)
+    o_ref, lse_ref, a = _oracle_fp8pv(q, k, v, causal, scale)
+    _check(o, lse, o_ref, lse_ref, a, f"fp8pv d=128 N={N} causal={causal}")
+
+
 def test_closed_form_zero_queries(gpu_lib):
     """Q = 0: P is uniform over the visible keys, so O is the mean of the decoded V rows."""
     N, d = 300, 64
