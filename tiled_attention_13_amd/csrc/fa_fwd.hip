@@ -599,7 +599,7 @@ void fwd_pp_kernel(KParams p) {
     float m_run = kNegInf, l_run = 0.0f;
     float s[BN / 2];
     bf16x8 pf[BN / 16];
-    uint32_t pf8[BN / 8];                        // FP8 P*V: the lane's 32 P values as e4m3 codes
+    uint32_t pf8[BN / 8] = {};                   // FP8 P*V: the lane's 32 P values as e4m3 codes
     int p_scale = 127;                           // FP8 P*V: block exponent of those codes
 
     // per-lane LDS addresses of this lane's K row / e4m3 V^T row fragments in stage 0
@@ -751,10 +751,12 @@ void fwd_pp_kernel(KParams p) {
                 for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
         }
         if constexpr (PV8) {
-            // byte t of the B operand is s[t] (register order = the k-slot order of f8_slot)
+            // byte t of the B operand is s[t] (register order = the k-slot order of f8_slot);
+            // the two packs overwrite both halves of the previous tile's word, which is
+            // passed as the preserved half so that no zero has to be written first
 #pragma unroll
             for (int wd = 0; wd < BN / 8; ++wd) {
-                int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[4 * wd], s[4 * wd + 1], 0, false);
+                int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[4 * wd], s[4 * wd + 1], static_cast<int>(pf8[wd]), false);
                 x = __builtin_amdgcn_cvt_pk_fp8_f32(s[4 * wd + 2], s[4 * wd + 3], x, true);
                 pf8[wd] = static_cast<uint32_t>(x);
             }
@@ -1057,7 +1059,7 @@ void fwd_b128_kernel(KParams p) {
     float m_run = kNegInf, l_run = 0.0f;
     float s[BN / 2];
     bf16x8 pf[BN / 16];
-    uint32_t pf8[2][8];                           // e4m3 P*V: P^T of each 64-key half, e4m3 codes
+    uint32_t pf8[2][8] = {};                      // e4m3 P*V: P^T of each 64-key half, e4m3 codes
     int p_scale[2] = {127, 127};                  // and their block exponents (127 - f)
 
     const uint8_t* lane_k = smem + l32 * C::KROW + 16 * h;
@@ -1211,7 +1213,8 @@ void fwd_b128_kernel(KParams p) {
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                 for (int wd = 0; wd < 8; ++wd) {
-                    int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[32 * hf + 4 * wd], s[32 * hf + 4 * wd + 1], 0, false);
+                    int x = __builtin_amdgcn_cvt_pk_fp8_f32(s[32 * hf + 4 * wd], s[32 * hf + 4 * wd + 1],
+                                                            static_cast<int>(pf8[hf][wd]), false);   // both halves rewritten
                     x = __builtin_amdgcn_cvt_pk_fp8_f32(s[32 * hf + 4 * wd + 2], s[32 * hf + 4 * wd + 3], x, true);
                     pf8[hf][wd] = static_cast<uint32_t>(x);
                 }
