@@ -77,7 +77,11 @@ typedef enum {
                          power-of-two scale (see fa_quant_v_pow2), P per
                          (query, 64-key tile) with a power-of-two scale
                          inside the kernel; both scales are the MFMA's own
-                         block exponents, so dequantisation is exact */
+                         block exponents, so dequantisation is exact.  V
+                         must be finite: at d = 128, when N mod 128 lies in
+                         1..64, the missing half of the last 128-key tile
+                         meets the next V^T row's codes with P = 0, and a
+                         NaN there would reach another column of O */
     /* not dtypes: they widen the enumeration so that any int a caller
        passes is a valid value of it (reported as FA_ERR_INVALID_DTYPE) */
     FA_DTYPE_MIN_ENUM = -0x7FFFFFFF - 1,
