@@ -667,8 +667,9 @@ void fwd_pp_kernel(KParams p) {
                     const u32x4 b0 = qf[2 * i], b1 = qf[2 * i + 1];
                     const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3],
                                      (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
-                    // fp8 e4m3 x fp8 e4m3, unit block scales (E8M0 127 = 2^0)
-                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+                    // fp8 e4m3 x fp8 e4m3, plain products: with both scale operands 0 the
+                    // compiler emits the unscaled v_mfma_f32_32x32x64_f8f6f4 (no scale load)
+                    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 0, 0, 0);
                 } else if constexpr (C::F8N) {
                     const long a = __builtin_bit_cast(long, *reinterpret_cast<const u32x2*>(krow + 16 * i + 8 * h));
                     const long b = __builtin_bit_cast(long, u32x2{qf[i][0], qf[i][1]});
@@ -1097,9 +1098,10 @@ void fwd_b128_kernel(KParams p) {
                 const u32x4 b0 = qf[2 * i], b1 = qf[2 * i + 1];
                 const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
 #pragma unroll
-                for (int kb = 0; kb < BN / 32; ++kb)   // e4m3 x e4m3, unit block scales (E8M0 127 = 2^0)
+                for (int kb = 0; kb < BN / 32; ++kb)   // e4m3 x e4m3, plain products (scale operands 0:
+                                                        // the unscaled v_mfma_f32_32x32x64_f8f6f4)
                     acc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i * (BN / 32) + kb], b, acc[kb], 0, 0, 0,
-                                                                              127, 0, 127);
+                                                                              0, 0, 0);
             }
             pipeline_lds_mfma<NA, C::AHEAD / 2, 2>();
 #pragma unroll
