@@ -446,6 +446,9 @@ def bench_fp8(steps: int):
     # mixed ceiling: Q.K^T (half the FLOPs) at the fp8 peak, P.V at the bf16 peak
     mixed = 1.0 / (0.5 / PEAK_TFLOPS["fp8"] + 0.5 / PEAK_TFLOPS["bf16"])
     res["fp8"]["prepass_ms"] = round(float(pre.mean()), 4)
+    from tiled_attention_13_amd import quant_v_pow2
+    pre_pv = _time_calls(lambda: (quant_fp8(q), quant_fp8(k), quant_v_pow2(v)), steps)
+    res["fp8pv"]["prepass_ms"] = round(float(pre_pv.mean()), 4)
     # vector-ALU estimate: the same per-score cost as the small-d floors (one FMA, one
     # exp, one add, half a bf16 pack; the FP8 softmax skips the row max while the
     # reference holds) over the causal half of the scores, at 2.4 GHz; in the
@@ -467,7 +470,8 @@ def bench_fp8(steps: int):
         res["fp8pv"]["counters"] = {k: t[k] for k in ("mfma_busy", "lds_bank_conflict_share",
                                                       "hbm_bytes_per_launch", "kernel_ms_under_profiler")}
     res["note"] = ("fp8: Q.K^T on e4m3, P.V on bf16; fp8pv: both on e4m3; ms_per_call includes the "
-                   "quantisation pre-passes, kernel_only is fa_fwd_fp8 on pre-quantised Q/K")
+                   "quantisation pre-passes (prepass_ms: those pre-passes alone, Q and K; fp8pv also V), "
+                   "kernel_only is fa_fwd_fp8 on pre-quantised Q/K")
     return res
 
 
